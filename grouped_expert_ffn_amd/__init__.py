@@ -1,0 +1,288 @@
+"""Python binding of the MI355X MoE token-dispatch library (libmoe_dispatch.so).
+
+Argument marshalling only: each function checks the torch tensors it is
+given (device, dtype, shape, contiguity), passes their device pointers and
+torch's current HIP stream to the C entry point of the same name, and raises
+``MoeError`` on a non-zero status. All arithmetic runs in the library's HIP
+kernels; torch provides device memory and streams. There is no fallback:
+importing this package fails loudly when the library has not been built.
+
+The layer: y_t = sum over e in TopK(h_t W_r, k) of g_{t,e} f_e(h_t)
+("How Does Mixture-of-Experts Routing Affect LLM Repeatability?", token-choice
+layer formula), staged as route -> permute -> grouped FFN -> unpermute/combine.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_dispatch.so")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+GATES = {"softmax": 0, "softmax_topk_renorm": 1, "sigmoid_topk_renorm": 2}
+ACTS = {"relu": 0, "swiglu": 1}
+FLAG_ROW_OVERFLOW, FLAG_BAD_EXPERT_ID, FLAG_NONFINITE_LOGIT, FLAG_DROPPED = 1, 2, 4, 8
+
+EXPORTED = ("moe_capacity_from_factor", "moe_workspace_size", "moe_route",
+            "moe_topk_from_logits", "moe_permute", "moe_grouped_ffn",
+            "moe_unpermute_combine", "moe_layer_forward", "moe_status_str")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {status_str(status)}")
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("gate", ctypes.c_int32), ("act", ctypes.c_int32), ("ep_size", ctypes.c_int32),
+                ("ep_rank", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("capacity", ctypes.c_int64), ("max_rows", ctypes.c_int64)]
+
+
+class LayerBuffers(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "logits", "topk_idx", "topk_gate", "counts", "offsets", "dest", "src_token",
+        "src_slot", "send_splits", "send_displs", "x_perm", "y_perm", "flags")]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m grouped_expert_ffn_amd.build` "
+            "(no CPU fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    D = ctypes.POINTER(LayerDesc)
+    sig = {
+        "moe_capacity_from_factor": (I64, [ctypes.c_double, I64, I32, I32]),
+        "moe_workspace_size": (I32, [D, ctypes.POINTER(SZ)]),
+        "moe_route": (I32, [D, P, P, P, P, P, P, P, P, SZ, P]),
+        "moe_topk_from_logits": (I32, [D, P, P, P, P, P]),
+        "moe_permute": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "moe_grouped_ffn": (I32, [D, P, P, P, P, P, P, SZ, P]),
+        "moe_unpermute_combine": (I32, [D, P, P, P, P, P, P]),
+        "moe_layer_forward": (I32, [D, P, P, P, P, P, P, ctypes.POINTER(LayerBuffers), P, SZ, P]),
+        "moe_status_str": (ctypes.c_char_p, [I32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+
+
+def status_str(status: int) -> str:
+    return _lib.moe_status_str(status).decode()
+
+
+def capacity_from_factor(cf, T: int, k: int, E: int) -> int:
+    """floor(cf*T*k/E), or -1 (dropless) when cf is None."""
+    return int(_lib.moe_capacity_from_factor(-1.0 if cf is None else float(cf), T, k, E))
+
+
+def make_desc(T, d, E, k, d_ff, dtype, gate, act, *, ep_size=1, ep_rank=0, capacity=-1,
+              max_rows=None) -> LayerDesc:
+    if isinstance(dtype, torch.dtype):
+        dtype = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}[dtype]
+    elif isinstance(dtype, str):
+        dtype = {"f32": DTYPE_F32, "bf16": DTYPE_BF16}[dtype]
+    return LayerDesc(T=T, d=d, E=E, k=k, d_ff=d_ff, dtype=dtype,
+                     gate=GATES[gate] if isinstance(gate, str) else gate,
+                     act=ACTS[act] if isinstance(act, str) else act,
+                     ep_size=ep_size, ep_rank=ep_rank, reserved=0,
+                     capacity=-1 if capacity is None else capacity,
+                     max_rows=T * k if max_rows is None else max_rows)
+
+
+def torch_dtype(desc: LayerDesc) -> torch.dtype:
+    return torch.bfloat16 if desc.dtype == DTYPE_BF16 else torch.float32
+
+
+def workspace_size(desc: LayerDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.moe_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "moe_workspace_size")
+    return int(n.value)
+
+
+def alloc_workspace(desc: LayerDesc, device="cuda") -> torch.Tensor:
+    # torch's caching allocator hands out 512-byte aligned blocks
+    return torch.empty(max(1, workspace_size(desc)), dtype=torch.uint8, device=device)
+
+
+def _check(status, where):
+    if status != 0:
+        raise MoeError(status, where)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t, name, dtype=None, shape=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ws(ws):
+    return _ptr(ws, "ws", torch.uint8), ctypes.c_size_t(ws.numel())
+
+
+@dataclass
+class LayerBuffersT:
+    """Device tensors of every output and intermediate of the layer."""
+    logits: torch.Tensor
+    topk_idx: torch.Tensor
+    topk_gate: torch.Tensor
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    dest: torch.Tensor
+    src_token: torch.Tensor
+    src_slot: torch.Tensor
+    send_splits: torch.Tensor
+    send_displs: torch.Tensor
+    x_perm: torch.Tensor
+    y_perm: torch.Tensor
+    flags: torch.Tensor
+
+
+def alloc_buffers(desc: LayerDesc, device="cuda") -> LayerBuffersT:
+    T, E, k, d, R = desc.T, desc.E, desc.k, desc.d, desc.max_rows
+    dt = torch_dtype(desc)
+    i32, f32 = torch.int32, torch.float32
+    return LayerBuffersT(
+        logits=torch.empty((T, E), dtype=f32, device=device),
+        topk_idx=torch.empty((T, k), dtype=i32, device=device),
+        topk_gate=torch.empty((T, k), dtype=f32, device=device),
+        counts=torch.empty((E,), dtype=i32, device=device),
+        offsets=torch.empty((E + 1,), dtype=i32, device=device),
+        dest=torch.empty((T, k), dtype=i32, device=device),
+        src_token=torch.full((max(R, 1),), -1, dtype=i32, device=device)[:R],
+        src_slot=torch.full((max(R, 1),), -1, dtype=i32, device=device)[:R],
+        send_splits=torch.empty((desc.ep_size,), dtype=torch.int64, device=device),
+        send_displs=torch.empty((desc.ep_size,), dtype=torch.int64, device=device),
+        x_perm=torch.empty((R, d), dtype=dt, device=device),
+        y_perm=torch.empty((R, d), dtype=dt, device=device),
+        flags=torch.zeros((1,), dtype=torch.int32, device=device),
+    )
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI, without the moe_ prefix)
+
+def route(desc, h, w_router, bias, logits, topk_idx, topk_gate, flags, ws, stream=None):
+    dt = torch_dtype(desc)
+    T, d, E, k = desc.T, desc.d, desc.E, desc.k
+    wsp, wsn = _ws(ws)
+    _check(_lib.moe_route(
+        ctypes.byref(desc), _ptr(h, "h", dt, (T, d)), _ptr(w_router, "w_router", dt, (d, E)),
+        _ptr(bias, "router_bias", torch.float32, (E,), optional=True),
+        _ptr(logits, "logits", torch.float32, (T, E)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
+        _ptr(topk_gate, "topk_gate", torch.float32, (T, k)),
+        _ptr(flags, "flags", torch.int32, (1,)), wsp, wsn, _stream(stream)), "moe_route")
+
+
+def topk_from_logits(desc, logits, topk_idx, topk_gate, flags, stream=None):
+    T, E, k = desc.T, desc.E, desc.k
+    _check(_lib.moe_topk_from_logits(
+        ctypes.byref(desc), _ptr(logits, "logits", torch.float32, (T, E)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
+        _ptr(topk_gate, "topk_gate", torch.float32, (T, k)),
+        _ptr(flags, "flags", torch.int32, (1,)), _stream(stream)), "moe_topk_from_logits")
+
+
+def permute(desc, h, topk_idx, x_perm, counts, offsets, dest, src_token, src_slot,
+            send_splits, send_displs, flags, ws, stream=None):
+    dt = torch_dtype(desc)
+    T, d, E, k, R = desc.T, desc.d, desc.E, desc.k, desc.max_rows
+    wsp, wsn = _ws(ws)
+    _check(_lib.moe_permute(
+        ctypes.byref(desc), _ptr(h, "h", dt, (T, d)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
+        _ptr(x_perm, "x_perm", dt, (R, d)), _ptr(counts, "counts", torch.int32, (E,)),
+        _ptr(offsets, "offsets", torch.int32, (E + 1,)),
+        _ptr(dest, "dest", torch.int32, (T, k)),
+        _ptr(src_token, "src_token", torch.int32, (R,)),
+        _ptr(src_slot, "src_slot", torch.int32, (R,)),
+        _ptr(send_splits, "send_splits", torch.int64, (desc.ep_size,)),
+        _ptr(send_displs, "send_displs", torch.int64, (desc.ep_size,)),
+        _ptr(flags, "flags", torch.int32, (1,)), wsp, wsn, _stream(stream)), "moe_permute")
+
+
+def _w_shapes(desc):
+    el = desc.E // desc.ep_size
+    rows = 2 * desc.d_ff if desc.act == ACTS["swiglu"] else desc.d_ff
+    return (el, rows, desc.d), (el, desc.d, desc.d_ff)
+
+
+def grouped_ffn(desc, x_perm, offsets, w1, w2, y_perm, ws, stream=None):
+    dt = torch_dtype(desc)
+    s1, s2 = _w_shapes(desc)
+    R, d = desc.max_rows, desc.d
+    wsp, wsn = _ws(ws)
+    _check(_lib.moe_grouped_ffn(
+        ctypes.byref(desc), _ptr(x_perm, "x_perm", dt, (R, d)),
+        _ptr(offsets, "offsets", torch.int32, (desc.E + 1,)),
+        _ptr(w1, "w1", dt, s1), _ptr(w2, "w2", dt, s2), _ptr(y_perm, "y_perm", dt, (R, d)),
+        wsp, wsn, _stream(stream)), "moe_grouped_ffn")
+
+
+def unpermute_combine(desc, y_perm, topk_idx, topk_gate, dest, y, stream=None):
+    dt = torch_dtype(desc)
+    T, d, k, R = desc.T, desc.d, desc.k, desc.max_rows
+    _check(_lib.moe_unpermute_combine(
+        ctypes.byref(desc), _ptr(y_perm, "y_perm", dt, (R, d)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
+        _ptr(topk_gate, "topk_gate", torch.float32, (T, k)),
+        _ptr(dest, "dest", torch.int32, (T, k)), _ptr(y, "y", dt, (T, d)),
+        _stream(stream)), "moe_unpermute_combine")
+
+
+def layer_forward(desc, h, w_router, bias, w1, w2, y, bufs: LayerBuffersT, ws, stream=None):
+    dt = torch_dtype(desc)
+    T, d, E, k, R = desc.T, desc.d, desc.E, desc.k, desc.max_rows
+    s1, s2 = _w_shapes(desc)
+    b = LayerBuffers(
+        logits=_ptr(bufs.logits, "logits", torch.float32, (T, E)).value,
+        topk_idx=_ptr(bufs.topk_idx, "topk_idx", torch.int32, (T, k)).value,
+        topk_gate=_ptr(bufs.topk_gate, "topk_gate", torch.float32, (T, k)).value,
+        counts=_ptr(bufs.counts, "counts", torch.int32, (E,)).value,
+        offsets=_ptr(bufs.offsets, "offsets", torch.int32, (E + 1,)).value,
+        dest=_ptr(bufs.dest, "dest", torch.int32, (T, k)).value,
+        src_token=_ptr(bufs.src_token, "src_token", torch.int32, (R,)).value,
+        src_slot=_ptr(bufs.src_slot, "src_slot", torch.int32, (R,)).value,
+        send_splits=_ptr(bufs.send_splits, "send_splits", torch.int64, (desc.ep_size,)).value,
+        send_displs=_ptr(bufs.send_displs, "send_displs", torch.int64, (desc.ep_size,)).value,
+        x_perm=_ptr(bufs.x_perm, "x_perm", dt, (R, d)).value,
+        y_perm=_ptr(bufs.y_perm, "y_perm", dt, (R, d)).value,
+        flags=_ptr(bufs.flags, "flags", torch.int32, (1,)).value)
+    wsp, wsn = _ws(ws)
+    _check(_lib.moe_layer_forward(
+        ctypes.byref(desc), _ptr(h, "h", dt, (T, d)), _ptr(w_router, "w_router", dt, (d, E)),
+        _ptr(bias, "router_bias", torch.float32, (E,), optional=True),
+        _ptr(w1, "w1", dt, s1), _ptr(w2, "w2", dt, s2), _ptr(y, "y", dt, (T, d)),
+        ctypes.byref(b), wsp, wsn, _stream(stream)), "moe_layer_forward")

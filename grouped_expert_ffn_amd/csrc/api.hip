@@ -1,0 +1,266 @@
+// C ABI entry points: argument validation on the host, then kernel launches
+// enqueued on the caller's stream. Nothing here synchronises, copies device
+// data to the host or allocates memory.
+#include "common.h"
+
+#define MOE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace moe {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static size_t elt_bytes(int dtype) { return dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+Workspace workspace_layout(const moe_layer_desc_t& d) {
+  Workspace w{};
+  size_t off = 0;
+  w.wrt = off;
+  if (d.dtype == MOE_DTYPE_BF16) off += align256((size_t)router_n_pad(d.E) * d.d * 2);
+  w.tile_hist = off;
+  const int64_t n_tiles = (d.T + kTokTile - 1) / kTokTile;
+  off += align256((size_t)n_tiles * d.E * 4);
+  w.gemm_tiles = off;
+  off += align256((size_t)(gemm_max_mtiles(d) + 1) * sizeof(int4));
+  w.act = off;
+  off += align256((size_t)d.max_rows * d.d_ff * elt_bytes(d.dtype));
+  w.total = off;
+  return w;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static moe_status_t check_desc(const moe_layer_desc_t* d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->dtype != MOE_DTYPE_F32 && d->dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if (d->gate < MOE_GATE_SOFTMAX || d->gate > MOE_GATE_SIGMOID_TOPK_RENORM)
+    return MOE_ERR_UNSUPPORTED;
+  if (d->act != MOE_ACT_RELU && d->act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
+  if (d->reserved != 0) return MOE_ERR_SHAPE;
+  if (d->T < 0 || d->d < 1 || d->d_ff < 1) return MOE_ERR_SHAPE;
+  if (d->E < 1 || d->E > kMaxE) return MOE_ERR_SHAPE;
+  if (d->k < 1 || d->k > kMaxK || d->k > d->E) return MOE_ERR_SHAPE;
+  if (d->ep_size < 1 || d->E % d->ep_size != 0) return MOE_ERR_SHAPE;
+  if (d->ep_rank < 0 || d->ep_rank >= d->ep_size) return MOE_ERR_SHAPE;
+  if (d->max_rows < 0 || d->max_rows >= (int64_t)1 << 31) return MOE_ERR_SHAPE;
+  if (d->T * (int64_t)d->k >= (int64_t)1 << 31) return MOE_ERR_SHAPE;
+  if (d->dtype == MOE_DTYPE_BF16 && (d->d % 64 != 0 || d->d_ff % 64 != 0)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+static moe_status_t check_ws(const moe_layer_desc_t* d, void* ws, size_t ws_bytes) {
+  const size_t need = workspace_layout(*d).total;
+  if (need == 0) return MOE_OK;
+  if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+struct Buf {
+  const void* p;
+  int64_t n;     // elements; a zero-size buffer may be NULL
+  bool data;     // element type is `dtype` (needs 16-byte alignment for bf16)
+};
+
+static moe_status_t check_bufs(const moe_layer_desc_t* d, std::initializer_list<Buf> bs) {
+  for (const Buf& b : bs) {
+    if (b.n == 0) continue;
+    if (!b.p) return MOE_ERR_NULL;
+    if (((uintptr_t)b.p & 3u) != 0) return MOE_ERR_ALIGN;
+    if (b.data && d->dtype == MOE_DTYPE_BF16 && !aligned16(b.p)) return MOE_ERR_ALIGN;
+  }
+  return MOE_OK;
+}
+
+#define MOE_TRY(x)                     \
+  do {                                 \
+    moe_status_t st__ = (x);           \
+    if (st__ != MOE_OK) return st__;   \
+  } while (0)
+
+#define HIP_TRY(x)                                \
+  do {                                            \
+    if ((x) != hipSuccess) return MOE_ERR_HIP;    \
+  } while (0)
+
+static moe_status_t do_route(const moe_layer_desc_t& d, const void* h, const void* w_router,
+                             const float* bias, float* logits, int32_t* idx, float* gate,
+                             uint32_t* flags, char* ws, hipStream_t s) {
+  if (d.dtype == MOE_DTYPE_BF16) {
+    const Workspace w = workspace_layout(d);
+    bf16* wt = reinterpret_cast<bf16*>(ws + w.wrt);
+    const int E_pad = router_n_pad(d.E);
+    HIP_TRY(launch_transpose_router_bf16((const bf16*)w_router, wt, d.d, d.E, E_pad, s));
+    HIP_TRY(launch_router_bf16((const bf16*)h, wt, bias, logits, d.T, d.d, d.E, E_pad, s));
+  } else {
+    HIP_TRY(launch_router_f32((const float*)h, (const float*)w_router, bias, logits, d.T, d.d,
+                              d.E, s));
+  }
+  HIP_TRY(launch_topk(logits, idx, gate, flags, d.T, d.E, d.k, d.gate, s));
+  return MOE_OK;
+}
+
+static moe_status_t do_permute(const moe_layer_desc_t& d, const void* h, const int32_t* idx,
+                               void* x_perm, int32_t* counts, int32_t* offsets, int32_t* dest,
+                               int32_t* src_token, int32_t* src_slot, int64_t* splits,
+                               int64_t* displs, uint32_t* flags, char* ws, hipStream_t s) {
+  const Workspace w = workspace_layout(d);
+  int32_t* tile_hist = reinterpret_cast<int32_t*>(ws + w.tile_hist);
+  HIP_TRY(launch_dispatch_plan(idx, tile_hist, counts, offsets, dest, src_token, src_slot, splits,
+                               displs, flags, d.T, d.E, d.k, d.capacity, d.max_rows, d.ep_size,
+                               s));
+  HIP_TRY(launch_permute_rows(h, dest, x_perm, d.T, d.k, (int)(d.d * elt_bytes(d.dtype)), s));
+  return MOE_OK;
+}
+
+static moe_status_t do_ffn(const moe_layer_desc_t& d, const void* x_perm, const int32_t* offsets,
+                           const void* w1, const void* w2, void* y_perm, char* ws,
+                           hipStream_t s) {
+  const Workspace w = workspace_layout(d);
+  if (d.max_rows == 0) return MOE_OK;
+  HIP_TRY(launch_grouped_ffn(d, x_perm, offsets, w1, w2, y_perm, ws + w.act,
+                             reinterpret_cast<int4*>(ws + w.gemm_tiles), s));
+  return MOE_OK;
+}
+
+static moe_status_t do_combine(const moe_layer_desc_t& d, const void* y_perm, const int32_t* idx,
+                               const float* gate, const int32_t* dest, void* y, hipStream_t s) {
+  const int el = d.E / d.ep_size;
+  HIP_TRY(launch_combine(y_perm, idx, gate, dest, y, d.T, d.k, d.d, d.dtype, d.ep_rank * el,
+                         (d.ep_rank + 1) * el, s));
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+MOE_EXPORT int64_t moe_capacity_from_factor(double cf, int64_t T, int32_t k, int32_t E) {
+  if (!(cf > 0.0) || E <= 0) return -1;
+  // floor(cf * T * k / E), evaluated in double like the definition reads
+  double c = cf * (double)T * (double)k / (double)E;
+  return (int64_t)c;
+}
+
+MOE_EXPORT moe_status_t moe_workspace_size(const moe_layer_desc_t* desc, size_t* bytes) {
+  MOE_TRY(check_desc(desc));
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = workspace_layout(*desc).total;
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status_t moe_route(const moe_layer_desc_t* desc, const void* h,
+                                  const void* w_router, const float* router_bias, float* logits,
+                                  int32_t* topk_idx, float* topk_gate, uint32_t* flags, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_layer_desc_t& d = *desc;
+  const int64_t TE = d.T * d.E, Tk = d.T * d.k;
+  MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {w_router, (int64_t)d.d * d.E, true},
+                            {logits, TE, false}, {topk_idx, Tk, false}, {topk_gate, Tk, false},
+                            {flags, 1, false}}));
+  if (router_bias && ((uintptr_t)router_bias & 3u)) return MOE_ERR_ALIGN;
+  MOE_TRY(check_ws(desc, ws, ws_bytes));
+  return do_route(*desc, h, w_router, router_bias, logits, topk_idx, topk_gate, flags,
+                  (char*)ws, (hipStream_t)stream);
+}
+
+MOE_EXPORT moe_status_t moe_topk_from_logits(const moe_layer_desc_t* desc, const float* logits,
+                                             int32_t* topk_idx, float* topk_gate,
+                                             uint32_t* flags, void* stream) {
+  MOE_TRY(check_desc(desc));
+  const int64_t TE = desc->T * desc->E, Tk = desc->T * desc->k;
+  MOE_TRY(check_bufs(desc, {{logits, TE, false}, {topk_idx, Tk, false}, {topk_gate, Tk, false},
+                            {flags, 1, false}}));
+  HIP_TRY(launch_topk(logits, topk_idx, topk_gate, flags, desc->T, desc->E, desc->k, desc->gate,
+                      (hipStream_t)stream));
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status_t moe_permute(const moe_layer_desc_t* desc, const void* h,
+                                    const int32_t* topk_idx, void* x_perm, int32_t* counts,
+                                    int32_t* offsets, int32_t* dest, int32_t* src_token,
+                                    int32_t* src_slot, int64_t* send_splits,
+                                    int64_t* send_displs, uint32_t* flags, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_layer_desc_t& d = *desc;
+  const int64_t Tk = d.T * d.k, R = d.max_rows;
+  MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {x_perm, R * d.d, true}, {topk_idx, Tk, false},
+                            {counts, d.E, false}, {offsets, d.E + 1, false}, {dest, Tk, false},
+                            {src_token, R, false}, {src_slot, R, false}, {flags, 1, false},
+                            {send_splits, d.ep_size, false}, {send_displs, d.ep_size, false}}));
+  MOE_TRY(check_ws(desc, ws, ws_bytes));
+  return do_permute(*desc, h, topk_idx, x_perm, counts, offsets, dest, src_token, src_slot,
+                    send_splits, send_displs, flags, (char*)ws, (hipStream_t)stream);
+}
+
+MOE_EXPORT moe_status_t moe_grouped_ffn(const moe_layer_desc_t* desc, const void* x_perm,
+                                        const int32_t* offsets, const void* w1, const void* w2,
+                                        void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_layer_desc_t& d = *desc;
+  const int64_t R = d.max_rows, el = d.E / d.ep_size;
+  const int64_t w1n = el * (d.act == MOE_ACT_SWIGLU ? 2 : 1) * d.d_ff * d.d, w2n = el * d.d * d.d_ff;
+  MOE_TRY(check_bufs(desc, {{x_perm, R * d.d, true}, {y_perm, R * d.d, true}, {w1, w1n, true},
+                            {w2, w2n, true}, {offsets, d.E + 1, false}}));
+  MOE_TRY(check_ws(desc, ws, ws_bytes));
+  return do_ffn(*desc, x_perm, offsets, w1, w2, y_perm, (char*)ws, (hipStream_t)stream);
+}
+
+MOE_EXPORT moe_status_t moe_unpermute_combine(const moe_layer_desc_t* desc, const void* y_perm,
+                                              const int32_t* topk_idx, const float* topk_gate,
+                                              const int32_t* dest, void* y, void* stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_layer_desc_t& d = *desc;
+  const int64_t Tk = d.T * d.k;
+  MOE_TRY(check_bufs(desc, {{y_perm, d.max_rows * d.d, true}, {y, d.T * d.d, true},
+                            {topk_idx, Tk, false}, {topk_gate, Tk, false}, {dest, Tk, false}}));
+  return do_combine(*desc, y_perm, topk_idx, topk_gate, dest, y, (hipStream_t)stream);
+}
+
+MOE_EXPORT moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const void* h,
+                                          const void* w_router, const float* router_bias,
+                                          const void* w1, const void* w2, void* y,
+                                          const moe_layer_buffers_t* b, void* ws,
+                                          size_t ws_bytes, void* stream) {
+  MOE_TRY(check_desc(desc));
+  if (!b) return MOE_ERR_NULL;
+  const moe_layer_desc_t& d = *desc;
+  {
+    const int64_t TE = d.T * d.E, Tk = d.T * d.k, R = d.max_rows, el = d.E / d.ep_size;
+    const int64_t w1n = el * (d.act == MOE_ACT_SWIGLU ? 2 : 1) * d.d_ff * d.d;
+    const int64_t w2n = el * d.d * d.d_ff;
+    MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {w_router, (int64_t)d.d * d.E, true},
+                              {w1, w1n, true}, {w2, w2n, true}, {y, d.T * d.d, true},
+                              {b->x_perm, R * d.d, true}, {b->y_perm, R * d.d, true},
+                              {b->logits, TE, false}, {b->topk_idx, Tk, false},
+                              {b->topk_gate, Tk, false}, {b->counts, d.E, false},
+                              {b->offsets, d.E + 1, false}, {b->dest, Tk, false},
+                              {b->src_token, R, false}, {b->src_slot, R, false},
+                              {b->send_splits, d.ep_size, false},
+                              {b->send_displs, d.ep_size, false}, {b->flags, 1, false}}));
+  }
+  if (router_bias && ((uintptr_t)router_bias & 3u)) return MOE_ERR_ALIGN;
+  MOE_TRY(check_ws(desc, ws, ws_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  MOE_TRY(do_route(d, h, w_router, router_bias, b->logits, b->topk_idx, b->topk_gate, b->flags,
+                   w, s));
+  MOE_TRY(do_permute(d, h, b->topk_idx, b->x_perm, b->counts, b->offsets, b->dest, b->src_token,
+                     b->src_slot, b->send_splits, b->send_displs, b->flags, w, s));
+  MOE_TRY(do_ffn(d, b->x_perm, b->offsets, w1, w2, b->y_perm, w, s));
+  return do_combine(d, b->y_perm, b->topk_idx, b->topk_gate, b->dest, y, s);
+}
+
+MOE_EXPORT const char* moe_status_str(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "inconsistent or unsupported sizes";
+    case MOE_ERR_ALIGN: return "a buffer is misaligned (bf16 buffers need 16 bytes)";
+    case MOE_ERR_DTYPE: return "unknown dtype";
+    case MOE_ERR_UNSUPPORTED: return "unknown gate or activation mode";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "a HIP kernel launch failed";
+  }
+  return "unknown status";
+}

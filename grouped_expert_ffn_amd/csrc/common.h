@@ -1,0 +1,61 @@
+// Internal declarations shared by the HIP translation units of the MoE
+// dispatch library (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_dispatch.h"
+
+namespace moe {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kTokTile = 128;   // tokens per dispatch tile (histogram / rank kernels)
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 16;
+
+// Workspace layout, shared by moe_workspace_size and the entry points.
+struct Workspace {
+  size_t wrt;        // router weight transposed to [E_pad, d] bf16 (bf16 route only)
+  size_t tile_hist;  // [n_tiles, E] int32 per-tile expert counts, then their prefixes
+  size_t gemm_tiles; // [max_mtiles] int4 grouped-GEMM tile table + count
+  size_t act;        // [max_rows, d_ff] dtype: SwiGLU/ReLU activations
+  size_t total;
+};
+
+Workspace workspace_layout(const moe_layer_desc_t& d);
+int router_n_pad(int E);
+int64_t gemm_max_mtiles(const moe_layer_desc_t& d);
+
+// ---- launchers (return hipSuccess or the launch error) ----
+hipError_t launch_transpose_router_bf16(const bf16* w, bf16* wt, int d, int E, int E_pad,
+                                        hipStream_t s);
+hipError_t launch_router_bf16(const bf16* h, const bf16* wt, const float* bias, float* logits,
+                              int64_t T, int d, int E, int E_pad, hipStream_t s);
+hipError_t launch_router_f32(const float* h, const float* w, const float* bias, float* logits,
+                             int64_t T, int d, int E, hipStream_t s);
+hipError_t launch_topk(const float* logits, int32_t* idx, float* gate, uint32_t* flags,
+                       int64_t T, int E, int k, int gate_mode, hipStream_t s);
+
+hipError_t launch_dispatch_plan(const int32_t* idx, int32_t* tile_hist, int32_t* counts,
+                                int32_t* offsets, int32_t* dest, int32_t* src_token,
+                                int32_t* src_slot, int64_t* send_splits, int64_t* send_displs,
+                                uint32_t* flags, int64_t T, int E, int k, int64_t capacity,
+                                int64_t max_rows, int ep_size, hipStream_t s);
+hipError_t launch_permute_rows(const void* h, const int32_t* dest, void* x_perm, int64_t T,
+                               int k, int row_bytes, hipStream_t s);
+hipError_t launch_combine(const void* y_perm, const int32_t* idx, const float* gate,
+                          const int32_t* dest, void* y, int64_t T, int k, int d, int dtype,
+                          int e_lo, int e_hi, hipStream_t s);
+
+hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
+                              const int32_t* offsets, const void* w1, const void* w2,
+                              void* y_perm, void* act, int4* tiles, hipStream_t s);
+
+}  // namespace moe

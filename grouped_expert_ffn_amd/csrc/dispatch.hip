@@ -1,0 +1,364 @@
+// Permute plan, row permute and unpermute + combine.
+//
+// The plan follows "MoE Token Dispatch: Why an All-Reduce Result Does Not
+// Describe the Exchange", section "Follow one documented dispatch and return
+// path" (per-expert counts and communication splits from the routing map,
+// tokens rearranged into per-expert groups, outputs restored to their
+// origin) and the capacity rule of "How does dropless MoE dispatch differ
+// from capacity factor token dropping?" (section "Why per-expert buffers
+// exist in expert-parallel training"): an expert keeps at most `capacity`
+// assignments; the repeatability page has capacity resolved in request
+// order, read here as ascending (token, slot) order.
+//
+// Everything stays on the device: a tile histogram, one scan workgroup, a
+// stable in-tile rank by wave ballots, then bandwidth-bound row copies. All
+// integer results are independent of scheduling (the only atomics are
+// integer counts and flag ORs).
+#include "common.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// 1. Per-tile expert histogram of the (token, slot) assignments.
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ idx,
+                                                   int32_t* __restrict__ tile_hist, int64_t T,
+                                                   int E, int k, uint32_t* __restrict__ flags) {
+  __shared__ int32_t h[kMaxE];
+  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  const int64_t a0 = (int64_t)blockIdx.x * kTokTile * k;
+  const int64_t a1 = min(T * k, a0 + (int64_t)kTokTile * k);
+  bool bad = false;
+  for (int64_t a = a0 + threadIdx.x; a < a1; a += 256) {
+    int e = idx[a];
+    if (e >= 0 && e < E)
+      atomicAdd(&h[e], 1);
+    else
+      bad = true;
+  }
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flags, MOE_FLAG_BAD_EXPERT_ID);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) tile_hist[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// ---------------------------------------------------------------------------
+// 2. One workgroup: tile counts -> exclusive prefix over tiles (in place),
+//    counts, capacity, offsets, expert-parallel splits, flags.
+//    Each expert's tiles are split into P parts so all 1024 threads work.
+__global__ __launch_bounds__(1024) void scan_kernel(
+    int32_t* __restrict__ tile_hist, int n_tiles, int E, int64_t capacity, int64_t max_rows,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int64_t* __restrict__ send_splits, int64_t* __restrict__ send_displs, int ep_size,
+    uint32_t* __restrict__ flags) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t kept[1024];
+  __shared__ int32_t any_drop;
+  const int tid = threadIdx.x;
+  const int P = 1024 / E;  // parts per expert (E <= 1024)
+  const int e = tid % E, p = tid / E;
+  const bool worker = p < P;
+  const int per = (n_tiles + P - 1) / P;
+  const int t0 = min(n_tiles, p * per), t1 = min(n_tiles, t0 + per);
+  if (tid == 0) any_drop = 0;
+  int32_t s = 0;
+  if (worker)
+    for (int t = t0; t < t1; ++t) s += tile_hist[(int64_t)t * E + e];
+  part[tid] = s;
+  __syncthreads();
+  int32_t base = 0;
+  if (worker) {
+    for (int q = 0; q < p; ++q) base += part[q * E + e];
+    int32_t run = base;
+    for (int t = t0; t < t1; ++t) {
+      int64_t i = (int64_t)t * E + e;
+      int32_t v = tile_hist[i];
+      tile_hist[i] = run;
+      run += v;
+    }
+  }
+  // totals per expert, from the last part's prefix + its own sum
+  if (worker && p == P - 1) {
+    int32_t total = base + s;
+    counts[e] = total;
+    int32_t kp = (capacity >= 0 && (int64_t)total > capacity) ? (int32_t)capacity : total;
+    if (kp < total) any_drop = 1;
+    kept[e] = kp;
+  }
+  __syncthreads();
+  // exclusive scan of kept over experts (Hillis-Steele, E <= 1024)
+  int32_t v = tid < E ? kept[tid] : 0;
+  part[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int32_t add = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  if (tid < E) offsets[tid] = part[tid] - v;
+  if (tid == E - 1) {
+    offsets[E] = part[tid];
+    uint32_t f = 0;
+    if (any_drop) f |= MOE_FLAG_DROPPED;
+    if ((int64_t)part[tid] > max_rows) f |= MOE_FLAG_ROW_OVERFLOW;
+    if (f) atomicOr(flags, f);
+  }
+  __syncthreads();
+  if (tid < ep_size) {
+    const int el = E / ep_size;
+    int32_t lo = tid * el == 0 ? 0 : part[tid * el - 1];
+    int32_t hi = part[(tid + 1) * el - 1];
+    send_displs[tid] = lo;
+    send_splits[tid] = hi - lo;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. Stable rank inside each tile (one wave per tile). 64 assignments at a
+//    time in (token, slot) order: lanes holding the same expert find each
+//    other by matching the expert id bit by bit with ballots; a lane's rank
+//    is the number of matching lanes below it, added to the expert's running
+//    position (the prefix over earlier tiles, then updated by the highest
+//    matching lane).
+__global__ __launch_bounds__(64) void rank_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ tile_prefix,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ dest,
+    int32_t* __restrict__ src_token, int32_t* __restrict__ src_slot, int64_t T, int E, int k,
+    int ebits, int64_t capacity, int64_t max_rows) {
+  __shared__ int32_t run[kMaxE];
+  __shared__ int32_t off[kMaxE];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) {
+    run[e] = tile_prefix[(int64_t)blockIdx.x * E + e];
+    off[e] = offsets[e];
+  }
+  __syncthreads();
+  const int64_t a0 = (int64_t)blockIdx.x * kTokTile * k;
+  const int64_t a1 = min(T * k, a0 + (int64_t)kTokTile * k);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t a = a0; a < a1; a += 64) {
+    const int64_t my = a + lane;
+    const bool in = my < a1;
+    const int e = in ? idx[my] : -1;
+    const bool valid = in && e >= 0 && e < E;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t ones = __ballot(bit);
+      peers &= bit ? ones : ~ones;
+    }
+    int pos = 0;
+    if (valid) {
+      const int rank = __popcll(peers & below);
+      const int base = run[e];
+      pos = base + rank;
+      const bool leader = (peers >> lane) == 1ull;  // highest lane of its group
+      if (leader) run[e] = base + __popcll(peers);
+    }
+    if (in) {
+      int32_t d = -1;
+      if (valid && (capacity < 0 || (int64_t)pos < capacity)) {
+        const int64_t row = (int64_t)off[e] + pos;
+        if (row >= max_rows) {
+          d = -2;
+        } else {
+          d = (int32_t)row;
+          src_token[row] = (int32_t)(my / k);
+          src_slot[row] = (int32_t)(my - (my / k) * k);
+        }
+      }
+      dest[my] = d;
+    }
+  }
+}
+
+hipError_t launch_dispatch_plan(const int32_t* idx, int32_t* tile_hist, int32_t* counts,
+                                int32_t* offsets, int32_t* dest, int32_t* src_token,
+                                int32_t* src_slot, int64_t* send_splits, int64_t* send_displs,
+                                uint32_t* flags, int64_t T, int E, int k, int64_t capacity,
+                                int64_t max_rows, int ep_size, hipStream_t s) {
+  const int n_tiles = (int)((T + kTokTile - 1) / kTokTile);
+  if (n_tiles > 0)
+    hipLaunchKernelGGL(hist_kernel, dim3(n_tiles), dim3(256), 0, s, idx, tile_hist, T, E, k,
+                       flags);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, tile_hist, n_tiles, E, capacity,
+                     max_rows, counts, offsets, send_splits, send_displs, ep_size, flags);
+  int ebits = 0;
+  while ((1 << ebits) < E) ++ebits;
+  if (n_tiles > 0)
+    hipLaunchKernelGGL(rank_kernel, dim3(n_tiles), dim3(64), 0, s, idx, tile_hist, offsets,
+                       dest, src_token, src_slot, T, E, k, ebits, capacity, max_rows);
+  return hipGetLastError();
+}
+
+int device_cu_count();
+
+// ---------------------------------------------------------------------------
+// 4. Row permute, token-major: one wave per token reads the row once in
+//    16-byte lanes and writes it to each of the token's materialised rows.
+template <int U>
+__global__ __launch_bounds__(256) void permute_rows_kernel(const u32x4* __restrict__ h,
+                                                           const int32_t* __restrict__ dest,
+                                                           u32x4* __restrict__ x, int64_t T,
+                                                           int k, int row_vec) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nw) {
+    const int mine = lane < k ? dest[t * k + lane] : -1;
+    int dj[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) dj[j] = __shfl(mine, j);
+    const u32x4* src = h + t * row_vec;
+    for (int c0 = lane; c0 < row_vec; c0 += 64 * U) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int c = c0 + u * 64;
+        if (c < row_vec) v[u] = __builtin_nontemporal_load(src + c);
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j >= k) break;
+        if (dj[j] < 0) continue;
+        u32x4* dst = x + (int64_t)dj[j] * row_vec;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          int c = c0 + u * 64;
+          if (c < row_vec) dst[c] = v[u];
+        }
+      }
+    }
+  }
+}
+
+// fp32 rows whose byte size is not a multiple of 16: plain 4-byte copies.
+__global__ __launch_bounds__(256) void permute_rows_f32_kernel(const float* __restrict__ h,
+                                                               const int32_t* __restrict__ dest,
+                                                               float* __restrict__ x, int64_t T,
+                                                               int k, int d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nw) {
+    for (int j = 0; j < k; ++j) {
+      int r = dest[t * k + j];
+      if (r < 0) continue;
+      for (int c = lane; c < d; c += 64) x[(int64_t)r * d + c] = h[t * d + c];
+    }
+  }
+}
+
+hipError_t launch_permute_rows(const void* h, const int32_t* dest, void* x_perm, int64_t T,
+                               int k, int row_bytes, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  int64_t blocks = min((T + 3) / 4, (int64_t)device_cu_count() * 8);
+  if (row_bytes % 16 == 0) {
+    hipLaunchKernelGGL(permute_rows_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const u32x4*)h, dest, (u32x4*)x_perm, T, k, row_bytes / 16);
+  } else {
+    hipLaunchKernelGGL(permute_rows_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const float*)h, dest, (float*)x_perm, T, k, row_bytes / 4);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 5. Unpermute + combine, token-major: one wave per token gathers its k
+//    rows, weights them by that token's own gates and sums in float32 in
+//    slot order, then rounds once.
+template <int U>
+__global__ __launch_bounds__(256) void combine_bf16_kernel(
+    const bf16x8* __restrict__ yp, const int32_t* __restrict__ idx,
+    const float* __restrict__ gate, const int32_t* __restrict__ dest, bf16x8* __restrict__ y,
+    int64_t T, int k, int row_vec, int e_lo, int e_hi) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nw) {
+    int mine = -1;
+    float gm = 0.f;
+    if (lane < k) {
+      int r = dest[t * k + lane];
+      int e = idx[t * k + lane];
+      if (r >= 0 && e >= e_lo && e < e_hi) {
+        mine = r;
+        gm = gate[t * k + lane];
+      }
+    }
+    int rj[kMaxK];
+    float gj[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      rj[j] = __shfl(mine, j);
+      gj[j] = __shfl(gm, j);
+    }
+    for (int c0 = lane; c0 < row_vec; c0 += 64 * U) {
+      float acc[U][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j >= k) break;
+        if (rj[j] < 0) continue;
+        const bf16x8* src = yp + (int64_t)rj[j] * row_vec;
+        bf16x8 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          int c = c0 + u * 64;
+          if (c < row_vec) v[u] = src[c];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(gj[j], (float)v[u][i], acc[u][i]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int c = c0 + u * 64;
+        if (c < row_vec) {
+          bf16x8 o;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[i] = (bf16)acc[u][i];
+          __builtin_nontemporal_store(o, y + t * row_vec + c);
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_f32_kernel(
+    const float* __restrict__ yp, const int32_t* __restrict__ idx,
+    const float* __restrict__ gate, const int32_t* __restrict__ dest, float* __restrict__ y,
+    int64_t T, int k, int d, int e_lo, int e_hi) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nw) {
+    for (int c = lane; c < d; c += 64) {
+      float acc = 0.f;
+      for (int j = 0; j < k; ++j) {
+        int r = dest[t * k + j];
+        int e = idx[t * k + j];
+        if (r >= 0 && e >= e_lo && e < e_hi) acc = fmaf(gate[t * k + j], yp[(int64_t)r * d + c], acc);
+      }
+      y[t * d + c] = acc;
+    }
+  }
+}
+
+hipError_t launch_combine(const void* y_perm, const int32_t* idx, const float* gate,
+                          const int32_t* dest, void* y, int64_t T, int k, int d, int dtype,
+                          int e_lo, int e_hi, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  int64_t blocks = min((T + 3) / 4, (int64_t)device_cu_count() * 8);
+  if (dtype == MOE_DTYPE_BF16) {
+    hipLaunchKernelGGL(combine_bf16_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const bf16x8*)y_perm, idx, gate, dest, (bf16x8*)y, T, k, d / 8, e_lo,
+                       e_hi);
+  } else {
+    hipLaunchKernelGGL(combine_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (const float*)y_perm, idx, gate, dest, (float*)y, T, k, d, e_lo, e_hi);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,209 @@
+// Grouped expert FFN over ragged groups: one launch per GEMM covers every
+// local expert's rows ("Dropless MoE Is a Runtime Problem as Much as a Model
+// Design", grouped GEMM paragraph: a collection of expert shapes in one
+// implementation, no per-expert launches, no padding to a common capacity).
+//
+// The group sizes live only on the device. A one-workgroup kernel turns the
+// expert offsets into a table of M-tiles (local expert, first row, end row);
+// the GEMM kernels are persistent grids that walk that table, so no host
+// sync and no padded rows. bf16 runs on MFMA with float32 accumulation; the
+// SwiGLU gate and up products share one pass over the activation tile and
+// are combined in float32 before the single bf16 rounding of `act`.
+#include "gemm_core.h"
+
+namespace moe {
+
+int device_cu_count();
+
+// ---------------------------------------------------------------------------
+// Tile table: for local expert i, rows [offsets[lo+i], offsets[lo+i+1])
+// clamped to max_rows, cut into BM-row tiles. Table length at the end.
+__global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets,
+                                                        int e_lo, int E_loc, int64_t max_rows,
+                                                        int BM, int4* __restrict__ tiles,
+                                                        int* __restrict__ n_tiles_out) {
+  __shared__ int scan[1024];
+  const int tid = threadIdx.x;
+  int r0 = 0, r1 = 0, mt = 0;
+  if (tid < E_loc) {
+    r0 = (int)min((int64_t)offsets[e_lo + tid], max_rows);
+    r1 = (int)min((int64_t)offsets[e_lo + tid + 1], max_rows);
+    mt = r1 > r0 ? (r1 - r0 + BM - 1) / BM : 0;
+  }
+  scan[tid] = mt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int add = tid >= o ? scan[tid - o] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  const int start = scan[tid] - mt;
+  for (int m = 0; m < mt; ++m) {
+    int a = r0 + m * BM;
+    tiles[start + m] = make_int4(tid, a, min(a + BM, r1), 0);
+  }
+  if (tid == 1023) *n_tiles_out = scan[1023];
+}
+
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ W, bf16* __restrict__ C,
+    const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr, int N, int K,
+    int64_t w_stride, int n_n, int64_t ldc) {
+  using TG = TileGemm<BM, BN, WM, WN, EPI>;
+  __shared__ __attribute__((aligned(16))) bf16 lds[TG::LDS_ELEMS];
+  const int n_m = *n_mt_ptr;
+  const int total = n_m * n_n;
+  const int G = gridDim.x;
+  for (int it = 0; it * G < total; ++it) {
+    const int v = xcd_virtual_id(blockIdx.x, G, it);
+    if (v >= total) continue;
+    int mt, nt;
+    tile_coords<8>(v, n_m, n_n, mt, nt);
+    const int4 t = tiles[mt];
+    TG::run(A, t.y, t.z - t.y, W + (int64_t)t.x * w_stride, nt * BN, N, K, C, ldc, nullptr, N,
+            lds);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+static hipError_t grouped_gemm_launch(const bf16* A, const bf16* W, bf16* C, const int4* tiles,
+                                      const int* n_mt, int N, int K, int64_t w_stride,
+                                      int64_t ldc, int64_t max_mtiles, int per_cu,
+                                      hipStream_t s) {
+  const int n_n = (N + BN - 1) / BN;
+  const int64_t ub = max_mtiles * n_n;
+  int64_t G = min(((ub + 7) / 8) * 8, (int64_t)device_cu_count() * per_cu);
+  G = max((int64_t)8, G / 8 * 8);
+  hipLaunchKernelGGL((grouped_gemm_kernel<BM, BN, WM, WN, EPI>), dim3((unsigned)G),
+                     dim3(64 * WM * WN), 0, s, A, W, C, tiles, n_mt, N, K, w_stride, n_n, ldc);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// float32 grouped GEMM (small layers): 64x64 output tiles, 256 threads each
+// computing a 4x4 block, K in slices of 16 through LDS. Epilogue 0 = store,
+// 1 = ReLU, 2 = SwiGLU (gate rows n, up rows N + n).
+constexpr int kF32BM = 64;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
+    const float* __restrict__ A, const float* __restrict__ W, float* __restrict__ C,
+    const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr, int N, int K,
+    int64_t w_stride, int64_t ldc) {
+  const int mt = blockIdx.x;
+  if (mt >= *n_mt_ptr) return;
+  const int4 t = tiles[mt];
+  const int rows = t.z - t.y;
+  const int n0 = blockIdx.y * 64;
+  const float* Wb = W + (int64_t)t.x * w_stride;
+  __shared__ float As[16][65], Bs[16][65], Us[16][65];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  float acc[4][4] = {}, accu[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    for (int q = threadIdx.x; q < 64 * 16; q += 256) {
+      int r = q >> 4, kk = q & 15;
+      int k = k0 + kk;
+      As[kk][r] = (r < rows && k < K) ? A[(int64_t)(t.y + r) * K + k] : 0.f;
+      int n = n0 + r;
+      Bs[kk][r] = (n < N && k < K) ? Wb[(int64_t)n * K + k] : 0.f;
+      if (EPI == 2) Us[kk][r] = (n < N && k < K) ? Wb[(int64_t)(N + n) * K + k] : 0.f;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4], u[4];
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+      if (EPI == 2)
+        for (int j = 0; j < 4; ++j) u[j] = Us[kk][tx * 4 + j];
+      for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+          if (EPI == 2) accu[i][j] = fmaf(a[i], u[j], accu[i][j]);
+        }
+    }
+    __syncthreads();
+  }
+  for (int i = 0; i < 4; ++i) {
+    int m = ty * 4 + i;
+    if (m >= rows) continue;
+    for (int j = 0; j < 4; ++j) {
+      int n = n0 + tx * 4 + j;
+      if (n >= N) continue;
+      float v = acc[i][j];
+      if (EPI == 1) v = fmaxf(v, 0.f);
+      if (EPI == 2) v = v / (1.0f + expf(-v)) * accu[i][j];
+      C[(int64_t)(t.y + m) * ldc + n] = v;
+    }
+  }
+}
+
+template <int EPI>
+static hipError_t grouped_gemm_f32_launch(const float* A, const float* W, float* C,
+                                          const int4* tiles, const int* n_mt, int N, int K,
+                                          int64_t w_stride, int64_t ldc, int64_t max_mtiles,
+                                          hipStream_t s) {
+  dim3 grid((unsigned)max_mtiles, (unsigned)((N + 63) / 64));
+  hipLaunchKernelGGL(grouped_gemm_f32_kernel<EPI>, grid, dim3(256), 0, s, A, W, C, tiles, n_mt,
+                     N, K, w_stride, ldc);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// bf16 tile shapes of the two expert GEMMs.
+constexpr int kG1_BM = 128, kG1_BN = 64, kG1_WM = 2, kG1_WN = 2;  // SwiGLU: 128 weight rows
+constexpr int kG2_BM = 128, kG2_BN = 128, kG2_WM = 2, kG2_WN = 2;
+
+int64_t gemm_max_mtiles(const moe_layer_desc_t& d) {
+  const int64_t el = d.E / d.ep_size;
+  const int64_t rows = d.max_rows;
+  return (rows + kF32BM - 1) / kF32BM + el;  // the smallest BM of any path
+}
+
+hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
+                              const int32_t* offsets, const void* w1, const void* w2,
+                              void* y_perm, void* act, int4* tiles, hipStream_t s) {
+  const int el = desc.E / desc.ep_size;
+  const int e_lo = desc.ep_rank * el;
+  const int64_t max_mt = gemm_max_mtiles(desc);
+  int* n_mt = reinterpret_cast<int*>(tiles + max_mt);
+  const int d = desc.d, dff = desc.d_ff;
+  const bool swiglu = desc.act == MOE_ACT_SWIGLU;
+  const int w1_rows = swiglu ? 2 * dff : dff;
+  hipError_t err;
+  if (desc.dtype == MOE_DTYPE_BF16) {
+    static_assert(kG1_BM == kG2_BM, "both GEMMs walk one tile table");
+    hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,
+                       desc.max_rows, kG1_BM, tiles, n_mt);
+    const int64_t mt_ub = (desc.max_rows + kG1_BM - 1) / kG1_BM + el;
+    const bf16* X = (const bf16*)x_perm;
+    bf16* H = (bf16*)act;
+    if (swiglu)
+      err = grouped_gemm_launch<kG1_BM, kG1_BN, kG1_WM, kG1_WN, EPI_SWIGLU_BF16>(
+          X, (const bf16*)w1, H, tiles, n_mt, dff, d, (int64_t)w1_rows * d, dff, mt_ub, 2, s);
+    else
+      err = grouped_gemm_launch<kG2_BM, kG2_BN, kG2_WM, kG2_WN, EPI_RELU_BF16>(
+          X, (const bf16*)w1, H, tiles, n_mt, dff, d, (int64_t)w1_rows * d, dff, mt_ub, 2, s);
+    if (err != hipSuccess) return err;
+    return grouped_gemm_launch<kG2_BM, kG2_BN, kG2_WM, kG2_WN, EPI_STORE_BF16>(
+        H, (const bf16*)w2, (bf16*)y_perm, tiles, n_mt, d, dff, (int64_t)d * dff, d, mt_ub, 2,
+        s);
+  }
+  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,
+                     desc.max_rows, kF32BM, tiles, n_mt);
+  const float* X = (const float*)x_perm;
+  float* H = (float*)act;
+  if (swiglu)
+    err = grouped_gemm_f32_launch<2>(X, (const float*)w1, H, tiles, n_mt, dff, d,
+                                     (int64_t)w1_rows * d, dff, max_mt, s);
+  else
+    err = grouped_gemm_f32_launch<1>(X, (const float*)w1, H, tiles, n_mt, dff, d,
+                                     (int64_t)w1_rows * d, dff, max_mt, s);
+  if (err != hipSuccess) return err;
+  return grouped_gemm_f32_launch<0>(H, (const float*)w2, (float*)y_perm, tiles, n_mt, d, dff,
+                                    (int64_t)d * dff, d, max_mt, s);
+}
+
+}  // namespace moe

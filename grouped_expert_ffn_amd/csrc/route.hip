@@ -1,0 +1,265 @@
+// Route: router scores s_t = h_t W_r (+ b), ordered top-k and gate weights.
+//
+// "How Does Mixture-of-Experts Routing Affect LLM Repeatability?", the
+// token-choice layer formula and its demand for stable score ordering with
+// deterministic tie handling: ids are ordered by score descending, equal
+// scores go to the lower expert id, -0 equals +0 and a NaN ranks below every
+// number (NaN or +-Inf raise MOE_FLAG_NONFINITE_LOGIT).
+#include "gemm_core.h"
+
+namespace moe {
+
+int router_n_pad(int E) {
+  if (E <= 16) return 16;
+  if (E <= 32) return 32;
+  if (E <= 64) return 64;
+  if (E <= 128) return 128;
+  return (E + 255) / 256 * 256;
+}
+
+// ---------------------------------------------------------------------------
+// W_r [d, E] -> W_r^T [E_pad, d] (rows E..E_pad-1 zero), so both router
+// operands are K-contiguous for the MFMA tile.
+__global__ __launch_bounds__(256) void transpose_router_kernel(const bf16* __restrict__ w,
+                                                               bf16* __restrict__ wt, int d,
+                                                               int E, int E_pad) {
+  __shared__ bf16 tile[32][33];
+  const int k0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int r = ty; r < 32; r += 8) {
+    int k = k0 + r, e = e0 + tx;
+    tile[r][tx] = (k < d && e < E) ? w[(int64_t)k * E + e] : (bf16)0.0f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    int e = e0 + r, k = k0 + tx;
+    if (e < E_pad && k < d) wt[(int64_t)e * d + k] = tile[tx][r];
+  }
+}
+
+hipError_t launch_transpose_router_bf16(const bf16* w, bf16* wt, int d, int E, int E_pad,
+                                        hipStream_t s) {
+  dim3 grid((d + 31) / 32, (E_pad + 31) / 32);
+  hipLaunchKernelGGL(transpose_router_kernel, grid, dim3(256), 0, s, w, wt, d, E, E_pad);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// bf16 router on MFMA: logits[T, E] = h[T, d] . W_r^T[E_pad, d]^T + bias.
+// Every token's dot products run over K in the same fixed slice order
+// whatever T is, so a token's scores do not depend on its batch.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void router_bf16_kernel(
+    const bf16* __restrict__ h, const bf16* __restrict__ wt, const float* __restrict__ bias,
+    float* __restrict__ logits, int64_t T, int d, int E, int E_pad, int n_m, int n_n) {
+  using TG = TileGemm<BM, BN, WM, WN, EPI_ROUTER_F32>;
+  __shared__ __attribute__((aligned(16))) bf16 lds[TG::LDS_ELEMS];
+  const int total = n_m * n_n;
+  const int G = gridDim.x;
+  for (int it = 0; it * G < total; ++it) {
+    int v = xcd_virtual_id(blockIdx.x, G, it);
+    if (v >= total) continue;
+    int mt, nt;
+    tile_coords<8>(v, n_m, n_n, mt, nt);
+    int64_t a0 = (int64_t)mt * BM;
+    int rows = (int)min((int64_t)BM, T - a0);
+    TG::run(h, a0, rows, wt, nt * BN, E_pad, d, logits, E, bias, E, lds);
+  }
+}
+
+static int g_num_cu[64];
+
+static int num_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!g_num_cu[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    g_num_cu[dev] = n;
+  }
+  return g_num_cu[dev];
+}
+
+int device_cu_count() { return num_cus(); }
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t router_launch(const bf16* h, const bf16* wt, const float* bias, float* logits,
+                                int64_t T, int d, int E, int E_pad, int per_cu, hipStream_t s) {
+  int n_m = (int)((T + BM - 1) / BM);
+  int n_n = E_pad / BN;
+  int total = n_m * n_n;
+  int G = min(((total + 7) / 8) * 8, num_cus() * per_cu);
+  G = max(8, G / 8 * 8);
+  hipLaunchKernelGGL((router_bf16_kernel<BM, BN, WM, WN>), dim3(G), dim3(64 * WM * WN), 0, s, h,
+                     wt, bias, logits, T, d, E, E_pad, n_m, n_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bf16(const bf16* h, const bf16* wt, const float* bias, float* logits,
+                              int64_t T, int d, int E, int E_pad, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  switch (E_pad) {
+    case 16: return router_launch<64, 16, 4, 1>(h, wt, bias, logits, T, d, E, E_pad, 4, s);
+    case 32: return router_launch<64, 32, 2, 2>(h, wt, bias, logits, T, d, E, E_pad, 4, s);
+    case 64: return router_launch<64, 64, 2, 2>(h, wt, bias, logits, T, d, E, E_pad, 4, s);
+    case 128: return router_launch<64, 128, 2, 2>(h, wt, bias, logits, T, d, E, E_pad, 2, s);
+    default: return router_launch<128, 256, 2, 4>(h, wt, bias, logits, T, d, E, E_pad, 1, s);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 router: one thread per (token, expert), K summed in order.
+__global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict__ h,
+                                                         const float* __restrict__ w,
+                                                         const float* __restrict__ bias,
+                                                         float* __restrict__ logits, int64_t T,
+                                                         int d, int E) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * E) return;
+  int64_t t = i / E;
+  int e = (int)(i - t * E);
+  const float* x = h + t * d;
+  float acc = 0.f;
+  for (int c = 0; c < d; ++c) acc = fmaf(x[c], w[(int64_t)c * E + e], acc);
+  if (bias) acc += bias[e];
+  logits[i] = acc;
+}
+
+hipError_t launch_router_f32(const float* h, const float* w, const float* bias, float* logits,
+                             int64_t T, int d, int E, hipStream_t s) {
+  int64_t n = T * E;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(router_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, h, w,
+                     bias, logits, T, d, E);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Top-k + gates. A token's E scores are spread over a segment of W lanes
+// (W = next power of two >= E, at most 64), V scores per lane. Each score
+// becomes a 64-bit key whose order is the ranking order: high 32 bits an
+// order-preserving image of the float (-0 folded onto +0, every NaN just
+// below -Inf, absent experts below that), low 32 bits the complemented id
+// so equal scores favour the lower id. k rounds of a segment max-reduction
+// pick the winners in order; keys are unique, so exactly one slot wins.
+__device__ __forceinline__ uint32_t score_bits(float x) {
+  if (x != x) return 1u;       // NaN: below every number
+  if (x == 0.0f) x = 0.0f;     // -0 -> +0
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int W>
+__device__ __forceinline__ uint64_t seg_max(uint64_t v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, W);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+template <int W>
+__device__ __forceinline__ float seg_sum(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
+  return v;
+}
+
+template <int W, int V>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+                                                   int32_t* __restrict__ idx,
+                                                   float* __restrict__ gate,
+                                                   uint32_t* __restrict__ flags, int64_t T, int E,
+                                                   int k, int mode) {
+  const int sl = threadIdx.x & (W - 1);
+  const int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) / W;
+  const bool act = t < T;
+  const float* row = logits + (act ? t : 0) * (int64_t)E;
+
+  float val[V];
+  uint64_t key[V];
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    int e = sl + i * W;
+    bool ok = act && e < E;
+    float x = ok ? row[e] : 0.0f;
+    val[i] = x;
+    bad |= ok && !isfinite(x);
+    key[i] = ok ? (((uint64_t)score_bits(x) << 32) | (uint32_t)(~(uint32_t)e)) : 0ull;
+  }
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flags, MOE_FLAG_NONFINITE_LOGIT);
+
+  uint32_t taken = 0;
+  uint64_t mine = 0;  // lane r < k keeps the key of the r-th winner
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (!(taken & (1u << i)) && key[i] > best) best = key[i];
+    uint64_t win = seg_max<W>(best);
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (key[i] == win && win != 0ull) taken |= 1u << i;
+    if (sl == r) mine = win;
+  }
+
+  const bool holder = act && sl < k;
+  const int my_id = (int)(~(uint32_t)(mine & 0xffffffffu));
+  const float my_v = holder ? row[my_id] : 0.0f;
+  float g = 0.f;
+  if (mode == MOE_GATE_SOFTMAX) {
+    float mx = __shfl(my_v, 0, W);  // the first winner holds the largest number
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      int e = sl + i * W;
+      if (act && e < E) part += __expf(val[i] - mx);
+    }
+    float sum = seg_sum<W>(part);
+    g = __expf(my_v - mx) / sum;
+  } else if (mode == MOE_GATE_SOFTMAX_TOPK_RENORM) {
+    float top = __shfl(my_v, 0, W);
+    float ex = holder ? __expf(my_v - top) : 0.f;
+    float sum = seg_sum<W>(ex);
+    g = ex / sum;
+  } else {
+    float sg = holder ? 1.0f / (1.0f + __expf(-my_v)) : 0.f;
+    float sum = seg_sum<W>(sg);
+    g = sg / sum;
+  }
+  if (holder) {
+    idx[t * k + sl] = my_id;
+    gate[t * k + sl] = g;
+  }
+}
+
+template <int W, int V>
+static hipError_t topk_launch(const float* logits, int32_t* idx, float* gate, uint32_t* flags,
+                              int64_t T, int E, int k, int mode, hipStream_t s) {
+  int64_t threads = T * W;
+  hipLaunchKernelGGL((topk_kernel<W, V>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     s, logits, idx, gate, flags, T, E, k, mode);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, int32_t* idx, float* gate, uint32_t* flags,
+                       int64_t T, int E, int k, int mode, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (E <= 1) return topk_launch<1, 1>(logits, idx, gate, flags, T, E, k, mode, s);
+  if (E <= 2) return topk_launch<2, 1>(logits, idx, gate, flags, T, E, k, mode, s);
+  if (E <= 4) return topk_launch<4, 1>(logits, idx, gate, flags, T, E, k, mode, s);
+  if (E <= 8) return topk_launch<8, 1>(logits, idx, gate, flags, T, E, k, mode, s);
+  if (E <= 16) return topk_launch<16, 1>(logits, idx, gate, flags, T, E, k, mode, s);
+  if (E <= 32) return topk_launch<32, 1>(logits, idx, gate, flags, T, E, k, mode, s);
+  if (E <= 64) return topk_launch<64, 1>(logits, idx, gate, flags, T, E, k, mode, s);
+  if (E <= 128) return topk_launch<64, 2>(logits, idx, gate, flags, T, E, k, mode, s);
+  if (E <= 256) return topk_launch<64, 4>(logits, idx, gate, flags, T, E, k, mode, s);
+  if (E <= 512) return topk_launch<64, 8>(logits, idx, gate, flags, T, E, k, mode, s);
+  return topk_launch<64, 16>(logits, idx, gate, flags, T, E, k, mode, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,206 @@
+/*
+ * moe_dispatch.h -- C ABI of the MI355X (gfx950) MoE token-dispatch layer.
+ *
+ * The layer computes, for every token t (the simplified token-choice layer of
+ * "How Does Mixture-of-Experts Routing Affect LLM Repeatability?"):
+ *
+ *     s_t = h_t W_r (+ b),   E_t = TopK(s_t, k),   y_t = sum_{e in E_t} g_{t,e} f_e(h_t)
+ *
+ * along the staged path of "MoE Token Dispatch: Why an All-Reduce Result Does
+ * Not Describe the Exchange", section "Follow one documented dispatch and
+ * return path": route -> per-expert counts and splits -> rows rearranged into
+ * per-expert groups -> experts -> outputs restored to their tokens.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument except `desc` and `ws_bytes`-style sizes is a
+ *    DEVICE pointer owned by the caller; the library allocates nothing, keeps
+ *    no state between calls and never frees caller memory.
+ *  - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *    the default stream). No entry point synchronises, copies device->host or
+ *    reads device data on the host, so every call can be captured in a graph.
+ *  - Row-major layouts. `dtype` (MOE_DTYPE_F32 or MOE_DTYPE_BF16) is the
+ *    element type of h, w_router, w1, w2, x_perm, y_perm and y. Logits and
+ *    gates are always float32; ids, counts, offsets, dest and the inverse map
+ *    are int32; expert-parallel splits are int64 (row units).
+ *  - Host-detectable argument errors return a non-zero moe_status_t before
+ *    anything is enqueued. Data-dependent conditions are OR-ed into the
+ *    caller-zeroed device word `flags` (MOE_FLAG_*); the caller reads it when
+ *    it chooses to (the periodic overflow check of "Dropless MoE Is a Runtime
+ *    Problem as Much as a Model Design", device-side metadata paragraph).
+ *  - A launch failure returns MOE_ERR_HIP; the HIP error is left for the
+ *    caller's next HIP call to report.
+ *  - `ws`/`ws_bytes`: caller-allocated device scratch of at least
+ *    moe_workspace_size() bytes, 256-byte aligned. Calls that share a
+ *    workspace must be ordered on one stream.
+ */
+#ifndef MOE_DISPATCH_H
+#define MOE_DISPATCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* inconsistent or unsupported sizes */
+  MOE_ERR_ALIGN = 3,       /* a bf16 buffer is not 16-byte aligned */
+  MOE_ERR_DTYPE = 4,       /* unknown dtype */
+  MOE_ERR_UNSUPPORTED = 5, /* unknown gate or activation mode */
+  MOE_ERR_WORKSPACE = 6,   /* workspace missing, misaligned or too small */
+  MOE_ERR_HIP = 7          /* a kernel launch failed */
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+/* Gate forms g_{t,e} of the chosen experts (the pages name g_{t,e}; the three
+ * forms are the ones the supported layers use). */
+typedef enum {
+  MOE_GATE_SOFTMAX = 0,             /* softmax over all E scores, not renormalised */
+  MOE_GATE_SOFTMAX_TOPK_RENORM = 1, /* softmax over the k chosen scores */
+  MOE_GATE_SIGMOID_TOPK_RENORM = 2  /* logistic(s) of the chosen, divided by their sum */
+} moe_gate_t;
+
+/* Expert map f_e. RELU: relu(x W1^T) W2^T with w1 [E_loc, d_ff, d].
+ * SWIGLU: (silu(x Wg^T) * (x Wu^T)) W2^T with w1 [E_loc, 2*d_ff, d] holding
+ * the gate rows Wg first, then the up rows Wu. w2 is [E_loc, d, d_ff]. */
+typedef enum { MOE_ACT_RELU = 0, MOE_ACT_SWIGLU = 1 } moe_act_t;
+
+/* Bits of the device flags word. */
+#define MOE_FLAG_ROW_OVERFLOW 1u    /* kept rows exceed max_rows; those rows get dest = -2 */
+#define MOE_FLAG_BAD_EXPERT_ID 2u   /* a (replayed) expert id outside [0, E); dest = -1 */
+#define MOE_FLAG_NONFINITE_LOGIT 4u /* a router score is NaN or +-Inf */
+#define MOE_FLAG_DROPPED 8u         /* capacity dropped at least one assignment (informational) */
+
+typedef struct moe_layer_desc {
+  int64_t T;        /* tokens, >= 0 */
+  int32_t d;        /* hidden width (bf16: multiple of 64) */
+  int32_t E;        /* experts, global count, 1..1024 */
+  int32_t k;        /* experts per token, 1..min(E, 16) */
+  int32_t d_ff;     /* expert inner width (bf16: multiple of 64) */
+  int32_t dtype;    /* moe_dtype_t */
+  int32_t gate;     /* moe_gate_t */
+  int32_t act;      /* moe_act_t */
+  int32_t ep_size;  /* expert-parallel ranks, >= 1, divides E */
+  int32_t ep_rank;  /* this GPU's rank; its local experts are
+                       [ep_rank*E/ep_size, (ep_rank+1)*E/ep_size) */
+  int32_t reserved; /* must be 0 */
+  int64_t capacity; /* per-expert cap; < 0 means dropless */
+  int64_t max_rows; /* rows allocated in x_perm / y_perm (T*k never overflows), < 2^31 */
+} moe_layer_desc_t;
+
+/* Per-expert capacity floor(cf * T * k / E) for a capacity factor cf > 0, or
+ * -1 (dropless) for cf <= 0. Capacity page ("How does dropless MoE dispatch
+ * differ from capacity factor token dropping?", section "Why per-expert
+ * buffers exist in expert-parallel training"), with the routed-assignment
+ * count T*k standing for the total tokens. Host-only, no device work. */
+int64_t moe_capacity_from_factor(double cf, int64_t T, int32_t k, int32_t E);
+
+/* Bytes of device workspace any entry point needs for `desc` (the fused call
+ * needs the most; the stage calls need no more). Host-only. */
+moe_status_t moe_workspace_size(const moe_layer_desc_t* desc, size_t* bytes);
+
+/* Route: logits[T,E] = h[T,d] . w_router[d,E] (+ router_bias[E]), then the
+ * ordered top-k ids (score descending, equal scores to the lower expert id,
+ * -0 == +0, NaN below every number) and their gates.
+ * Repeatability page: token-choice formula and the demand for stable score
+ * ordering with deterministic tie handling.
+ *   h          [T,d] dtype          w_router  [d,E] dtype
+ *   router_bias [E] float32 or NULL  logits   [T,E] float32 (written)
+ *   topk_idx   [T,k] int32 (written) topk_gate [T,k] float32 (written)
+ *   flags      [1] uint32, OR-ed with MOE_FLAG_NONFINITE_LOGIT
+ * Each token's scores are summed in an order that does not depend on T or
+ * on the other tokens, so a token routes the same alone or in any batch. */
+moe_status_t moe_route(const moe_layer_desc_t* desc, const void* h, const void* w_router,
+                       const float* router_bias, float* logits, int32_t* topk_idx,
+                       float* topk_gate, uint32_t* flags, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Top-k and gates only, from caller logits [T,E] float32 (same rules as
+ * moe_route). No workspace. */
+moe_status_t moe_topk_from_logits(const moe_layer_desc_t* desc, const float* logits,
+                                  int32_t* topk_idx, float* topk_gate, uint32_t* flags,
+                                  void* stream);
+
+/* Permute: group the (token, slot) assignments of topk_idx [T,k] by expert
+ * and copy the token rows into x_perm [max_rows,d].
+ * Dispatch page ("Follow one documented dispatch and return path"): counts
+ * and communication splits from the routing map, tokens rearranged per
+ * expert. Capacity page and the repeatability page's capacity passage: at
+ * most `capacity` assignments per expert are kept, overflow is dropped in
+ * ascending (token, slot) order.
+ *   counts   [E]   assignments per expert before capacity
+ *   offsets  [E+1] exclusive scan of min(counts, capacity): expert e owns
+ *                  rows offsets[e]..offsets[e+1]-1, members in (token, slot) order
+ *   dest     [T,k] row of each assignment; -1 dropped (capacity or bad id);
+ *                  -2 row >= max_rows (MOE_FLAG_ROW_OVERFLOW)
+ *   src_token, src_slot [max_rows] inverse map, written for rows
+ *                  0..min(offsets[E], max_rows)-1; later rows untouched
+ *   send_splits, send_displs [ep_size] rows and first row of each
+ *                  expert-parallel rank's contiguous segment (send buffers)
+ *   flags    OR-ed with BAD_EXPERT_ID, DROPPED, ROW_OVERFLOW
+ * Every output is bit-exact and independent of launch timing. */
+moe_status_t moe_permute(const moe_layer_desc_t* desc, const void* h, const int32_t* topk_idx,
+                         void* x_perm, int32_t* counts, int32_t* offsets, int32_t* dest,
+                         int32_t* src_token, int32_t* src_slot, int64_t* send_splits,
+                         int64_t* send_displs, uint32_t* flags, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Grouped expert FFN: for every local expert e, rows offsets[e]..offsets[e+1]-1
+ * (clamped to max_rows) of x_perm go through f_e into the same rows of y_perm
+ * [max_rows,d]; other rows of y_perm are untouched. One launch per GEMM over
+ * all ragged groups ("Dropless MoE Is a Runtime Problem as Much as a Model
+ * Design", grouped GEMM paragraph). bf16 runs on MFMA with float32
+ * accumulation; the SwiGLU product is formed in float32 and stored as bf16.
+ *   w1 [E_loc, d_ff or 2*d_ff, d], w2 [E_loc, d, d_ff] (local experts only) */
+moe_status_t moe_grouped_ffn(const moe_layer_desc_t* desc, const void* x_perm,
+                             const int32_t* offsets, const void* w1, const void* w2,
+                             void* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Unpermute + combine: y[t] = sum_j topk_gate[t,j] * y_perm[dest[t,j]] over
+ * slots with dest >= 0 whose expert is local, summed in float32 in slot
+ * order, rounded once to dtype. Tokens with no such slot get zeros (the
+ * residual is the caller's). Unpermute page ("moe-unpermute-wrong-token"):
+ * each row returns to its own token with that token's probability. */
+moe_status_t moe_unpermute_combine(const moe_layer_desc_t* desc, const void* y_perm,
+                                   const int32_t* topk_idx, const float* topk_gate,
+                                   const int32_t* dest, void* y, void* stream);
+
+/* Buffers of the fused call; all are required device pointers with the
+ * shapes given above. */
+typedef struct moe_layer_buffers {
+  float* logits;        /* [T,E] */
+  int32_t* topk_idx;    /* [T,k] */
+  float* topk_gate;     /* [T,k] */
+  int32_t* counts;      /* [E] */
+  int32_t* offsets;     /* [E+1] */
+  int32_t* dest;        /* [T,k] */
+  int32_t* src_token;   /* [max_rows] */
+  int32_t* src_slot;    /* [max_rows] */
+  int64_t* send_splits; /* [ep_size] */
+  int64_t* send_displs; /* [ep_size] */
+  void* x_perm;         /* [max_rows,d] dtype */
+  void* y_perm;         /* [max_rows,d] dtype */
+  uint32_t* flags;      /* [1], caller-zeroed */
+} moe_layer_buffers_t;
+
+/* The whole layer in one call: route, permute, grouped FFN, unpermute +
+ * combine, enqueued back to back on `stream` with no host synchronisation.
+ * Equivalent to the four stage calls in order. */
+moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const void* h, const void* w_router,
+                               const float* router_bias, const void* w1, const void* w2, void* y,
+                               const moe_layer_buffers_t* buffers, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_str(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DISPATCH_H */

@@ -350,11 +350,14 @@ def brute_force_tokens(h, w_router, bias, w1, w2, tokens, *, k, gate, act,
     lo = ep_rank * el
     tokens = list(tokens)
     last = max(tokens) if tokens else -1
-    need = range(0, last + 1) if capacity >= 0 else tokens
+    need = list(range(0, last + 1)) if capacity >= 0 else tokens
+    # scores of the tokens that take part (one row each; rows are independent)
+    s_all = router_logits(h[need], w_router, bias) if need else np.zeros((0, E))
+    row_of = {t: i for i, t in enumerate(need)}
     accepted = np.zeros(E, np.int64)
     kept_of = {}
     for t in need:
-        s = router_logits(h[t:t + 1], w_router, bias)
+        s = s_all[row_of[t]:row_of[t] + 1]
         if route_idx is None:
             ranked = sorted(range(E), key=lambda e: (-s[0, e], e))
             sel = ranked[:k]
@@ -370,10 +373,17 @@ def brute_force_tokens(h, w_router, bias, w1, w2, tokens, *, k, gate, act,
             else:
                 keep.append((j, e))
         kept_of[t] = (keep, g)
-    out = np.zeros((len(tokens), h.shape[1]), np.float64)
+    # y_t = sum of g_{t,e} f_e(h_t) over the kept local experts; each expert
+    # is evaluated once on the stack of sampled tokens that need it
+    uses = {}
     for i, t in enumerate(tokens):
         keep, g = kept_of[t]
         for j, e in keep:
             if lo <= e < lo + el:
-                out[i] += g[j] * expert_ffn(h[t:t + 1], w1[e - lo], w2[e - lo], act)[0]
+                uses.setdefault(e, []).append((i, t, g[j]))
+    out = np.zeros((len(tokens), h.shape[1]), np.float64)
+    for e, lst in uses.items():
+        f = expert_ffn(h[[t for _, t, _ in lst]], w1[e - lo], w2[e - lo], act)
+        for r, (i, _, gj) in enumerate(lst):
+            out[i] += gj * f[r]
     return out

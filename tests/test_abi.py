@@ -1,0 +1,96 @@
+"""The C ABI: the library loads, exports every function include/*.h declares,
+and its host-only paths (capacity, workspace size, status text, argument
+validation that returns before any launch) behave as documented. No GPU."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+
+def _declared():
+    names = set()
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def G():
+    from grouped_expert_ffn_amd import build as B
+    if not os.path.exists(B.LIB):
+        B.build()
+    import grouped_expert_ffn_amd as G
+    return G
+
+
+def test_every_declared_symbol_is_exported(G):
+    names = _declared()
+    assert names >= {"moe_route", "moe_permute", "moe_grouped_ffn", "moe_unpermute_combine",
+                     "moe_layer_forward", "moe_topk_from_logits", "moe_workspace_size",
+                     "moe_capacity_from_factor", "moe_status_str"}
+    lib = ctypes.CDLL(G.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert set(G.EXPORTED) == names
+
+
+def test_capacity_from_factor(G):
+    assert G.capacity_from_factor(1.0, 4096, 2, 8) == 1024
+    assert G.capacity_from_factor(1.25, 16384, 8, 128) == 1280
+    assert G.capacity_from_factor(1.0, 10, 1, 3) == 3
+    assert G.capacity_from_factor(None, 10, 1, 3) == -1
+
+
+def test_workspace_size_grows_with_rows(G):
+    a = G.workspace_size(G.make_desc(8192, 4096, 8, 2, 14336, "bf16", "softmax_topk_renorm", "swiglu"))
+    b = G.workspace_size(G.make_desc(4096, 4096, 8, 2, 14336, "bf16", "softmax_topk_renorm", "swiglu"))
+    assert a > b > 0 and a % 256 == 0
+    # the activation buffer dominates: max_rows * d_ff bf16
+    assert a >= 16384 * 14336 * 2
+
+
+def test_status_strings(G):
+    for s in range(8):
+        assert G.status_str(s)
+    assert G.status_str(0) == "ok"
+
+
+def _call_route(G, desc, h=1024, ws=None, ws_bytes=0):
+    lib = G._lib
+    p = ctypes.c_void_p
+    return lib.moe_route(ctypes.byref(desc) if desc is not None else None, p(h), p(1024), None,
+                         p(2048), p(4096), p(8192), p(16384), p(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("k", 0, 2), ("k", 17, 2), ("k", 9, 2), ("E", 2000, 2), ("ep_size", 3, 2),
+    ("ep_rank", 1, 2), ("dtype", 5, 4), ("gate", 9, 5), ("act", 7, 5), ("d", 100, 2),
+    ("d_ff", 96, 2), ("max_rows", 1 << 31, 2), ("reserved", 1, 2),
+])
+def test_bad_descriptors_rejected_before_launch(G, field, value, status):
+    desc = G.make_desc(64, 128, 8, 2, 128, "bf16", "softmax", "swiglu")
+    setattr(desc, field, value)
+    assert _call_route(G, desc) == status
+
+
+def test_null_and_alignment_and_workspace_errors(G):
+    desc = G.make_desc(64, 128, 8, 2, 128, "bf16", "softmax", "swiglu")
+    assert _call_route(G, None) == 1
+    assert _call_route(G, desc, h=0) == 1
+    assert _call_route(G, desc, h=1032) == 3           # bf16 data needs 16-byte alignment
+    assert _call_route(G, desc, ws=None) == 6           # workspace required
+    need = G.workspace_size(desc)
+    assert _call_route(G, desc, ws=256, ws_bytes=need - 1) == 6
+    assert _call_route(G, desc, ws=300, ws_bytes=need) == 6   # not 256-aligned
+
+
+def test_fp32_allows_any_width(G):
+    desc = G.make_desc(64, 30, 4, 2, 50, "f32", "softmax", "relu")
+    assert G.workspace_size(desc) > 0
