@@ -89,7 +89,7 @@ def main():
     ap.add_argument("--workload", default="mixtral_bf16")
     ap.add_argument("--cf", type=float, default=None, help="capacity factor (default dropless)")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "

@@ -82,6 +82,40 @@ static hipError_t grouped_gemm_launch(const bf16* A, const bf16* W, bf16* C, con
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int STAGES, int GROUP_M, int MF>
+__global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ W, bf16* __restrict__ C,
+    const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr, int N, int K,
+    int64_t w_stride, int n_n, int64_t ldc) {
+  using TG = TileGemmDL<BM, BN, WM, WN, EPI, BK, STAGES, MF>;
+  __shared__ __attribute__((aligned(1024))) bf16 lds[TG::LDS_ELEMS];
+  const int n_m = *n_mt_ptr;
+  const int total = n_m * n_n;
+  const int G = gridDim.x;
+  for (int it = 0; it * G < total; ++it) {
+    const int v = xcd_virtual_id(blockIdx.x, G, it);
+    if (v >= total) continue;
+    int mt, nt;
+    tile_coords<GROUP_M>(v, n_m, n_n, mt, nt);
+    const int4 t = tiles[mt];
+    TG::run(A, t.y, t.z - t.y, W + (int64_t)t.x * w_stride, nt * BN, N, K, C, ldc, lds);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int STAGES, int GROUP_M, int MF>
+static hipError_t grouped_gemm_dl_launch(const bf16* A, const bf16* W, bf16* C,
+                                         const int4* tiles, const int* n_mt, int N, int K,
+                                         int64_t w_stride, int64_t ldc, int64_t max_mtiles,
+                                         int per_cu, hipStream_t s) {
+  const int n_n = (N + BN - 1) / BN;
+  const int64_t ub = max_mtiles * n_n;
+  int64_t G = min(((ub + 7) / 8) * 8, (int64_t)device_cu_count() * per_cu);
+  G = max((int64_t)8, G / 8 * 8);
+  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BN, WM, WN, EPI, BK, STAGES, GROUP_M, MF>), dim3((unsigned)G),
+                     dim3(64 * WM * WN), 0, s, A, W, C, tiles, n_mt, N, K, w_stride, n_n, ldc);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // float32 grouped GEMM (small layers): 64x64 output tiles, 256 threads each
 // computing a 4x4 block, K in slices of 16 through LDS. Epilogue 0 = store,
@@ -152,9 +186,13 @@ static hipError_t grouped_gemm_f32_launch(const float* A, const float* W, float*
 }
 
 // ---------------------------------------------------------------------------
-// bf16 tile shapes of the two expert GEMMs.
-constexpr int kG1_BM = 128, kG1_BN = 64, kG1_WM = 2, kG1_WN = 2;  // SwiGLU: 128 weight rows
-constexpr int kG2_BM = 128, kG2_BN = 128, kG2_WM = 2, kG2_WN = 2;
+// bf16 expert GEMMs: 256-row M tiles, 8 waves (2 x 4), each wave a 128 x 64
+// block of 16x16x32 MFMAs; K slices of 64 stream into LDS by direct loads.
+// GEMM1 (SwiGLU) stages 128 gate + 128 up weight rows per tile and writes
+// 128 activation columns; GEMM2 stages 256 weight rows. Tiles are walked
+// 4 M-tiles per N column (GROUP_M = 4) in XCD-major order.
+constexpr int kGemmBM = 256;
+constexpr int kGemmGroupM = 4;
 
 int64_t gemm_max_mtiles(const moe_layer_desc_t& d) {
   const int64_t el = d.E / d.ep_size;
@@ -174,22 +212,20 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
   const int w1_rows = swiglu ? 2 * dff : dff;
   hipError_t err;
   if (desc.dtype == MOE_DTYPE_BF16) {
-    static_assert(kG1_BM == kG2_BM, "both GEMMs walk one tile table");
     hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,
-                       desc.max_rows, kG1_BM, tiles, n_mt);
-    const int64_t mt_ub = (desc.max_rows + kG1_BM - 1) / kG1_BM + el;
+                       desc.max_rows, kGemmBM, tiles, n_mt);
+    const int64_t mt_ub = (desc.max_rows + kGemmBM - 1) / kGemmBM + el;
     const bf16* X = (const bf16*)x_perm;
     bf16* H = (bf16*)act;
     if (swiglu)
-      err = grouped_gemm_launch<kG1_BM, kG1_BN, kG1_WM, kG1_WN, EPI_SWIGLU_BF16>(
-          X, (const bf16*)w1, H, tiles, n_mt, dff, d, (int64_t)w1_rows * d, dff, mt_ub, 2, s);
+      err = grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_SWIGLU_BF16, 64, 2, kGemmGroupM, 16>(
+          X, (const bf16*)w1, H, tiles, n_mt, dff, d, (int64_t)w1_rows * d, dff, mt_ub, 1, s);
     else
-      err = grouped_gemm_launch<kG2_BM, kG2_BN, kG2_WM, kG2_WN, EPI_RELU_BF16>(
-          X, (const bf16*)w1, H, tiles, n_mt, dff, d, (int64_t)w1_rows * d, dff, mt_ub, 2, s);
+      err = grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_RELU_BF16, 64, 2, kGemmGroupM, 16>(
+          X, (const bf16*)w1, H, tiles, n_mt, dff, d, (int64_t)w1_rows * d, dff, mt_ub, 1, s);
     if (err != hipSuccess) return err;
-    return grouped_gemm_launch<kG2_BM, kG2_BN, kG2_WM, kG2_WN, EPI_STORE_BF16>(
-        H, (const bf16*)w2, (bf16*)y_perm, tiles, n_mt, d, dff, (int64_t)d * dff, d, mt_ub, 2,
-        s);
+    return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_STORE_BF16, 64, 2, kGemmGroupM, 16>(
+        H, (const bf16*)w2, (bf16*)y_perm, tiles, n_mt, d, dff, (int64_t)d * dff, d, mt_ub, 1, s);
   }
   hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,
                      desc.max_rows, kF32BM, tiles, n_mt);
