@@ -18,7 +18,6 @@ from __future__ import annotations
 
 import argparse
 import hashlib
-import glob
 import json
 import os
 import re
@@ -39,10 +38,14 @@ def ffn_flops(n_rows, d, dff, act):
     return (6 if act == "swiglu" else 4) * n_rows * d * dff
 
 
+FFN_SOURCES = ("common.h", "gemm_core.h", "ffn.hip")
+
+
 def kernel_source_sha():
+    """Hash of the sources the grouped-FFN kernels are built from."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "grouped_expert_ffn_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
+    for name in FFN_SOURCES:
+        h.update(open(os.path.join(ROOT, "grouped_expert_ffn_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -90,6 +93,8 @@ def main():
     ap.add_argument("--cf", type=float, default=None, help="capacity factor (default dropless)")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
@@ -97,6 +102,17 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration_mib:
+        # a plain copy of known size: reads N bytes, writes N bytes per launch
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": 3}), flush=True)
+        return
     import grouped_expert_ffn_amd as G
     from workloads import CONFIGS, make_inputs
 

@@ -47,41 +47,6 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ W, bf16* __restrict__ C,
-    const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr, int N, int K,
-    int64_t w_stride, int n_n, int64_t ldc) {
-  using TG = TileGemm<BM, BN, WM, WN, EPI>;
-  __shared__ __attribute__((aligned(16))) bf16 lds[TG::LDS_ELEMS];
-  const int n_m = *n_mt_ptr;
-  const int total = n_m * n_n;
-  const int G = gridDim.x;
-  for (int it = 0; it * G < total; ++it) {
-    const int v = xcd_virtual_id(blockIdx.x, G, it);
-    if (v >= total) continue;
-    int mt, nt;
-    tile_coords<8>(v, n_m, n_n, mt, nt);
-    const int4 t = tiles[mt];
-    TG::run(A, t.y, t.z - t.y, W + (int64_t)t.x * w_stride, nt * BN, N, K, C, ldc, nullptr, N,
-            lds);
-  }
-}
-
-template <int BM, int BN, int WM, int WN, int EPI>
-static hipError_t grouped_gemm_launch(const bf16* A, const bf16* W, bf16* C, const int4* tiles,
-                                      const int* n_mt, int N, int K, int64_t w_stride,
-                                      int64_t ldc, int64_t max_mtiles, int per_cu,
-                                      hipStream_t s) {
-  const int n_n = (N + BN - 1) / BN;
-  const int64_t ub = max_mtiles * n_n;
-  int64_t G = min(((ub + 7) / 8) * 8, (int64_t)device_cu_count() * per_cu);
-  G = max((int64_t)8, G / 8 * 8);
-  hipLaunchKernelGGL((grouped_gemm_kernel<BM, BN, WM, WN, EPI>), dim3((unsigned)G),
-                     dim3(64 * WM * WN), 0, s, A, W, C, tiles, n_mt, N, K, w_stride, n_n, ldc);
-  return hipGetLastError();
-}
-
 template <int BM, int BN, int WM, int WN, int EPI, int BK, int STAGES, int GROUP_M, int MF>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, bf16* __restrict__ C,
