@@ -60,20 +60,33 @@ __global__ __launch_bounds__(1024) void scan_kernel(
   const int per = (n_tiles + P - 1) / P;
   const int t0 = min(n_tiles, p * per), t1 = min(n_tiles, t0 + per);
   if (tid == 0) any_drop = 0;
+  // each worker's column slice is read in batches of independent loads
+  constexpr int kB = 16;
   int32_t s = 0;
-  if (worker)
-    for (int t = t0; t < t1; ++t) s += tile_hist[(int64_t)t * E + e];
+  if (worker) {
+    for (int t = t0; t < t1; t += kB) {
+      int32_t v[kB];
+#pragma unroll
+      for (int i = 0; i < kB; ++i) v[i] = t + i < t1 ? tile_hist[(int64_t)(t + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kB; ++i) s += v[i];
+    }
+  }
   part[tid] = s;
   __syncthreads();
   int32_t base = 0;
   if (worker) {
     for (int q = 0; q < p; ++q) base += part[q * E + e];
     int32_t run = base;
-    for (int t = t0; t < t1; ++t) {
-      int64_t i = (int64_t)t * E + e;
-      int32_t v = tile_hist[i];
-      tile_hist[i] = run;
-      run += v;
+    for (int t = t0; t < t1; t += kB) {
+      int32_t v[kB];
+#pragma unroll
+      for (int i = 0; i < kB; ++i) v[i] = t + i < t1 ? tile_hist[(int64_t)(t + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kB; ++i) {
+        if (t + i < t1) tile_hist[(int64_t)(t + i) * E + e] = run;
+        run += v[i];
+      }
     }
   }
   // totals per expert, from the last part's prefix + its own sum
@@ -136,10 +149,22 @@ __global__ __launch_bounds__(64) void rank_kernel(
   const int64_t a0 = (int64_t)blockIdx.x * kTokTile * k;
   const int64_t a1 = min(T * k, a0 + (int64_t)kTokTile * k);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t a = a0; a < a1; a += 64) {
+  // the tile's ids, loaded up front so the serial matching loop below never
+  // waits on global memory (at most kTokTile * kMaxK / 64 per lane)
+  constexpr int kMaxIt = kTokTile * kMaxK / 64;
+  int ids[kMaxIt];
+#pragma unroll
+  for (int it = 0; it < kMaxIt; ++it) {
+    const int64_t my = a0 + (int64_t)it * 64 + lane;
+    ids[it] = my < a1 ? idx[my] : -1;
+  }
+#pragma unroll
+  for (int it = 0; it < kMaxIt; ++it) {
+    const int64_t a = a0 + (int64_t)it * 64;
+    if (a >= a1) break;
     const int64_t my = a + lane;
     const bool in = my < a1;
-    const int e = in ? idx[my] : -1;
+    const int e = ids[it];
     const bool valid = in && e >= 0 && e < E;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < ebits; ++b) {
@@ -172,19 +197,161 @@ __global__ __launch_bounds__(64) void rank_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// 3'. Scan folded into the rank step, for plans up to kFusedPlanMax tile x
+//     expert counts: every workgroup (one per tile) reduces the tile
+//     histograms itself -- each expert's total and its prefix over earlier
+//     tiles, with LDS integer atomics -- so no separate scan launch is needed.
+//     Workgroup 0 also writes counts, offsets, splits and flags. The ranking
+//     then runs as in rank_kernel, on wave 0.
+constexpr int64_t kFusedPlanMax = 1 << 12;
+
+__global__ __launch_bounds__(256) void rank_scan_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ tile_hist, int n_tiles,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ dest,
+    int32_t* __restrict__ src_token, int32_t* __restrict__ src_slot,
+    int64_t* __restrict__ send_splits, int64_t* __restrict__ send_displs, int ep_size,
+    uint32_t* __restrict__ flags, int64_t T, int E, int k, int ebits, int64_t capacity,
+    int64_t max_rows) {
+  __shared__ int32_t pre[kMaxE];       // prefix over earlier tiles, then the running position
+  __shared__ int32_t tot[kMaxE];       // per-expert totals
+  __shared__ int32_t off[kMaxE + 1];   // offsets
+  __shared__ int32_t wsum[256];
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x;
+  for (int e = tid; e < E; e += 256) {
+    pre[e] = 0;
+    tot[e] = 0;
+  }
+  __syncthreads();
+  const int n = n_tiles * E;            // <= kFusedPlanMax
+#pragma unroll 8
+  for (int i = tid; i < n; i += 256) {
+    const int v = tile_hist[i];
+    if (v) {
+      const int t = i / E, e = i - t * E;
+      atomicAdd(&tot[e], v);
+      if (t < tile) atomicAdd(&pre[e], v);
+    }
+  }
+  __syncthreads();
+  // exclusive scan over experts of min(total, capacity): each thread takes a
+  // run of consecutive experts, then the 256 run sums are scanned
+  const int per = (E + 255) / 256;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int32_t local = 0;
+  bool drop = false;
+  for (int e = e0; e < e1; ++e) {
+    const int32_t c = tot[e];
+    const int32_t kp = (capacity >= 0 && (int64_t)c > capacity) ? (int32_t)capacity : c;
+    drop |= kp < c;
+    local += kp;
+  }
+  wsum[tid] = local;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int32_t add = tid >= o ? wsum[tid - o] : 0;
+    __syncthreads();
+    wsum[tid] += add;
+    __syncthreads();
+  }
+  int32_t run0 = wsum[tid] - local;
+  for (int e = e0; e < e1; ++e) {
+    off[e] = run0;
+    const int32_t c = tot[e];
+    run0 += (capacity >= 0 && (int64_t)c > capacity) ? (int32_t)capacity : c;
+  }
+  if (tid == 255) off[E] = wsum[255];
+  const bool any_drop = __syncthreads_or(drop);
+  if (tile == 0) {
+    for (int e = tid; e < E; e += 256) {
+      counts[e] = tot[e];
+      offsets[e] = off[e];
+    }
+    if (tid == 0) {
+      offsets[E] = off[E];
+      uint32_t f = 0;
+      if (any_drop) f |= MOE_FLAG_DROPPED;
+      if ((int64_t)off[E] > max_rows) f |= MOE_FLAG_ROW_OVERFLOW;
+      if (f) atomicOr(flags, f);
+    }
+    if (tid < ep_size) {
+      const int el = E / ep_size;
+      send_displs[tid] = off[tid * el];
+      send_splits[tid] = off[(tid + 1) * el] - off[tid * el];
+    }
+  }
+  if (tid >= 64) return;
+
+  const int lane = tid;
+  const int64_t a0 = (int64_t)tile * kTokTile * k;
+  const int64_t a1 = min(T * k, a0 + (int64_t)kTokTile * k);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  constexpr int kMaxIt = kTokTile * kMaxK / 64;
+  int ids[kMaxIt];
+#pragma unroll
+  for (int it = 0; it < kMaxIt; ++it) {
+    const int64_t my = a0 + (int64_t)it * 64 + lane;
+    ids[it] = my < a1 ? idx[my] : -1;
+  }
+#pragma unroll
+  for (int it = 0; it < kMaxIt; ++it) {
+    const int64_t a = a0 + (int64_t)it * 64;
+    if (a >= a1) break;
+    const int64_t my = a + lane;
+    const bool in = my < a1;
+    const int e = ids[it];
+    const bool valid = in && e >= 0 && e < E;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t ones = __ballot(bit);
+      peers &= bit ? ones : ~ones;
+    }
+    int pos = 0;
+    if (valid) {
+      const int rank = __popcll(peers & below);
+      const int base = pre[e];
+      pos = base + rank;
+      const bool leader = (peers >> lane) == 1ull;  // highest lane of its group
+      if (leader) pre[e] = base + __popcll(peers);
+    }
+    if (in) {
+      int32_t d = -1;
+      if (valid && (capacity < 0 || (int64_t)pos < capacity)) {
+        const int64_t row = (int64_t)off[e] + pos;
+        if (row >= max_rows) {
+          d = -2;
+        } else {
+          d = (int32_t)row;
+          src_token[row] = (int32_t)(my / k);
+          src_slot[row] = (int32_t)(my - (my / k) * k);
+        }
+      }
+      dest[my] = d;
+    }
+  }
+}
+
 hipError_t launch_dispatch_plan(const int32_t* idx, int32_t* tile_hist, int32_t* counts,
                                 int32_t* offsets, int32_t* dest, int32_t* src_token,
                                 int32_t* src_slot, int64_t* send_splits, int64_t* send_displs,
                                 uint32_t* flags, int64_t T, int E, int k, int64_t capacity,
                                 int64_t max_rows, int ep_size, hipStream_t s) {
   const int n_tiles = (int)((T + kTokTile - 1) / kTokTile);
+  int ebits = 0;
+  while ((1 << ebits) < E) ++ebits;
   if (n_tiles > 0)
     hipLaunchKernelGGL(hist_kernel, dim3(n_tiles), dim3(256), 0, s, idx, tile_hist, T, E, k,
                        flags);
+  if ((int64_t)n_tiles * E <= kFusedPlanMax) {
+    hipLaunchKernelGGL(rank_scan_kernel, dim3(max(n_tiles, 1)), dim3(256), 0, s, idx, tile_hist,
+                       n_tiles, counts, offsets, dest, src_token, src_slot, send_splits,
+                       send_displs, ep_size, flags, T, E, k, ebits, capacity, max_rows);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, tile_hist, n_tiles, E, capacity,
                      max_rows, counts, offsets, send_splits, send_displs, ep_size, flags);
-  int ebits = 0;
-  while ((1 << ebits) < E) ++ebits;
   if (n_tiles > 0)
     hipLaunchKernelGGL(rank_kernel, dim3(n_tiles), dim3(64), 0, s, idx, tile_hist, offsets,
                        dest, src_token, src_slot, T, E, k, ebits, capacity, max_rows);
@@ -252,7 +419,7 @@ hipError_t launch_permute_rows(const void* h, const int32_t* dest, void* x_perm,
   if (T == 0) return hipSuccess;
   int64_t blocks = min((T + 3) / 4, (int64_t)device_cu_count() * 8);
   if (row_bytes % 16 == 0) {
-    hipLaunchKernelGGL(permute_rows_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL(permute_rows_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s,
                        (const u32x4*)h, dest, (u32x4*)x_perm, T, k, row_bytes / 16);
   } else {
     hipLaunchKernelGGL(permute_rows_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
@@ -349,9 +516,9 @@ hipError_t launch_combine(const void* y_perm, const int32_t* idx, const float* g
                           const int32_t* dest, void* y, int64_t T, int k, int d, int dtype,
                           int e_lo, int e_hi, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  int64_t blocks = min((T + 3) / 4, (int64_t)device_cu_count() * 8);
+  int64_t blocks = min((T + 3) / 4, (int64_t)device_cu_count() * 16);
   if (dtype == MOE_DTYPE_BF16) {
-    hipLaunchKernelGGL(combine_bf16_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL(combine_bf16_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s,
                        (const bf16x8*)y_perm, idx, gate, dest, (bf16x8*)y, T, k, d / 8, e_lo,
                        e_hi);
   } else {

@@ -5,6 +5,8 @@
 // deterministic tie handling: ids are ordered by score descending, equal
 // scores go to the lower expert id, -0 equals +0 and a NaN ranks below every
 // number (NaN or +-Inf raise MOE_FLAG_NONFINITE_LOGIT).
+#include <type_traits>
+
 #include "gemm_core.h"
 
 namespace moe {
@@ -46,24 +48,79 @@ hipError_t launch_transpose_router_bf16(const bf16* w, bf16* wt, int d, int E, i
 
 // ---------------------------------------------------------------------------
 // bf16 router on MFMA: logits[T, E] = h[T, d] . W_r^T[E_pad, d]^T + bias.
-// Every token's dot products run over K in the same fixed slice order
-// whatever T is, so a token's scores do not depend on its batch.
+// Every token's dot products run over K in an order fixed by E and d alone
+// (never by T or by the token's neighbours), so a token's scores do not
+// depend on its batch.
+//
+// E <= 32: one workgroup per 16 tokens; its eight waves take interleaved
+// 32-wide K steps, reading token and weight fragments straight from global
+// memory into 16x16x32 MFMAs, and the eight partial sums are added in wave
+// order through LDS. The token rows stream once with many loads in flight.
+constexpr int kSkinnyWaves = 8;
+
+template <int NB>
+__global__ __launch_bounds__(64 * kSkinnyWaves) void router_skinny_kernel(
+    const bf16* __restrict__ h, const bf16* __restrict__ wt, const float* __restrict__ bias,
+    float* __restrict__ logits, int64_t T, int d, int E) {
+  __shared__ f32x4 red[kSkinnyWaves][NB][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  int64_t tr = t0 + lr;
+  tr = tr < T ? tr : T - 1;
+  const bf16* hp = h + tr * d + lq * 8;
+  const bf16* wp = wt + (int64_t)lr * d + lq * 8;
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nks = d / 32;
+#pragma unroll 4
+  for (int ks = wave; ks < nks; ks += kSkinnyWaves) {
+    const bf16x8 hv = *reinterpret_cast<const bf16x8*>(hp + ks * 32);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const bf16x8 wv = *reinterpret_cast<const bf16x8*>(wp + (int64_t)b * 16 * d + ks * 32);
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, hv, acc[b], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) red[wave][b][lane] = acc[b];
+  __syncthreads();
+  if (wave == 0) {
+    const int64_t t = t0 + lr;
+    if (t < T) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        f32x4 sum = red[0][b][lane];
+#pragma unroll
+        for (int w = 1; w < kSkinnyWaves; ++w) sum += red[w][b][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = b * 16 + lq * 4 + i;   // lane holds experts 4*lq+i of token lr
+          if (e < E) logits[t * E + e] = sum[i] + (bias ? bias[e] : 0.0f);
+        }
+      }
+    }
+  }
+}
+
+// E >= 64: the direct-load MFMA tile with a float epilogue (bias added there).
 template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void router_bf16_kernel(
+__global__ __launch_bounds__(64 * WM * WN) void router_tile_kernel(
     const bf16* __restrict__ h, const bf16* __restrict__ wt, const float* __restrict__ bias,
     float* __restrict__ logits, int64_t T, int d, int E, int E_pad, int n_m, int n_n) {
-  using TG = TileGemm<BM, BN, WM, WN, EPI_ROUTER_F32>;
-  __shared__ __attribute__((aligned(16))) bf16 lds[TG::LDS_ELEMS];
+  using TG = TileGemmDL<BM, BN, WM, WN, EPI_ROUTER_F32, 64, 2, 16>;
+  __shared__ __attribute__((aligned(1024))) bf16 lds[TG::LDS_ELEMS];
   const int total = n_m * n_n;
   const int G = gridDim.x;
   for (int it = 0; it * G < total; ++it) {
-    int v = xcd_virtual_id(blockIdx.x, G, it);
+    const int v = xcd_virtual_id(blockIdx.x, G, it);
     if (v >= total) continue;
     int mt, nt;
     tile_coords<8>(v, n_m, n_n, mt, nt);
-    int64_t a0 = (int64_t)mt * BM;
-    int rows = (int)min((int64_t)BM, T - a0);
-    TG::run(h, a0, rows, wt, nt * BN, E_pad, d, logits, E, bias, E, lds);
+    const int64_t a0 = (int64_t)mt * BM;
+    const int rows = (int)min((int64_t)BM, T - a0);
+    TG::run(h, a0, rows, wt, nt * BN, E_pad, d, logits, E, lds, bias, E);
   }
 }
 
@@ -85,14 +142,15 @@ static int num_cus() {
 int device_cu_count() { return num_cus(); }
 
 template <int BM, int BN, int WM, int WN>
-static hipError_t router_launch(const bf16* h, const bf16* wt, const float* bias, float* logits,
-                                int64_t T, int d, int E, int E_pad, int per_cu, hipStream_t s) {
-  int n_m = (int)((T + BM - 1) / BM);
-  int n_n = E_pad / BN;
-  int total = n_m * n_n;
-  int G = min(((total + 7) / 8) * 8, num_cus() * per_cu);
+static hipError_t router_tile_launch(const bf16* h, const bf16* wt, const float* bias,
+                                     float* logits, int64_t T, int d, int E, int E_pad,
+                                     hipStream_t s) {
+  const int n_m = (int)((T + BM - 1) / BM);
+  const int n_n = E_pad / BN;
+  const int total = n_m * n_n;
+  int G = min(((total + 7) / 8) * 8, num_cus());
   G = max(8, G / 8 * 8);
-  hipLaunchKernelGGL((router_bf16_kernel<BM, BN, WM, WN>), dim3(G), dim3(64 * WM * WN), 0, s, h,
+  hipLaunchKernelGGL((router_tile_kernel<BM, BN, WM, WN>), dim3(G), dim3(64 * WM * WN), 0, s, h,
                      wt, bias, logits, T, d, E, E_pad, n_m, n_n);
   return hipGetLastError();
 }
@@ -100,12 +158,19 @@ static hipError_t router_launch(const bf16* h, const bf16* wt, const float* bias
 hipError_t launch_router_bf16(const bf16* h, const bf16* wt, const float* bias, float* logits,
                               int64_t T, int d, int E, int E_pad, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  const unsigned blocks16 = (unsigned)((T + 15) / 16);
   switch (E_pad) {
-    case 16: return router_launch<64, 16, 4, 1>(h, wt, bias, logits, T, d, E, E_pad, 4, s);
-    case 32: return router_launch<64, 32, 2, 2>(h, wt, bias, logits, T, d, E, E_pad, 4, s);
-    case 64: return router_launch<64, 64, 2, 2>(h, wt, bias, logits, T, d, E, E_pad, 4, s);
-    case 128: return router_launch<64, 128, 2, 2>(h, wt, bias, logits, T, d, E, E_pad, 2, s);
-    default: return router_launch<128, 256, 2, 4>(h, wt, bias, logits, T, d, E, E_pad, 1, s);
+    case 16:
+      hipLaunchKernelGGL(router_skinny_kernel<1>, dim3(blocks16), dim3(64 * kSkinnyWaves), 0, s, h, wt, bias,
+                         logits, T, d, E);
+      return hipGetLastError();
+    case 32:
+      hipLaunchKernelGGL(router_skinny_kernel<2>, dim3(blocks16), dim3(64 * kSkinnyWaves), 0, s, h, wt, bias,
+                         logits, T, d, E);
+      return hipGetLastError();
+    case 64: return router_tile_launch<64, 64, 2, 4>(h, wt, bias, logits, T, d, E, E_pad, s);
+    case 128: return router_tile_launch<64, 128, 2, 4>(h, wt, bias, logits, T, d, E, E_pad, s);
+    default: return router_tile_launch<128, 256, 2, 4>(h, wt, bias, logits, T, d, E, E_pad, s);
   }
 }
 
@@ -137,13 +202,15 @@ hipError_t launch_router_f32(const float* h, const float* w, const float* bias, 
 }
 
 // ---------------------------------------------------------------------------
-// Top-k + gates. A token's E scores are spread over a segment of W lanes
-// (W = next power of two >= E, at most 64), V scores per lane. Each score
-// becomes a 64-bit key whose order is the ranking order: high 32 bits an
-// order-preserving image of the float (-0 folded onto +0, every NaN just
-// below -Inf, absent experts below that), low 32 bits the complemented id
-// so equal scores favour the lower id. k rounds of a segment max-reduction
-// pick the winners in order; keys are unique, so exactly one slot wins.
+// Top-k + gates. A token's E scores are spread over a segment of W lanes, V
+// scores per lane (W = 16 for 16 < E <= 256, the next power of two >= E below
+// that, 64 above). Each score becomes a 64-bit key whose order is the ranking
+// order: high 32 bits an order-preserving image of the float (-0 folded onto
+// +0, every NaN just below -Inf, absent experts below that), low 32 bits the
+// complemented id so equal scores favour the lower id. k rounds of a segment
+// max-reduction pick the winners in order; keys are unique, so exactly one
+// slot wins each round. Segments of up to 16 lanes reduce with DPP row
+// permutations (no LDS traffic); 64-lane segments use cross-lane shuffles.
 __device__ __forceinline__ uint32_t score_bits(float x) {
   if (x != x) return 1u;       // NaN: below every number
   if (x == 0.0f) x = 0.0f;     // -0 -> +0
@@ -151,20 +218,55 @@ __device__ __forceinline__ uint32_t score_bits(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// inverse of score_bits for a present, non-NaN score
+__device__ __forceinline__ float bits_score(uint32_t b) {
+  return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+
+// DPP patterns that, applied in turn with a commutative op, leave every lane
+// of a W-lane segment (W <= 16, aligned in a 16-lane row) with the result.
+template <int W, typename F>
+__device__ __forceinline__ void seg_dpp_steps(F&& step) {
+  if (W >= 2) step(std::integral_constant<int, 0xB1>());   // quad_perm [1,0,3,2]
+  if (W >= 4) step(std::integral_constant<int, 0x4E>());   // quad_perm [2,3,0,1]
+  if (W >= 8) step(std::integral_constant<int, 0x141>());  // row_half_mirror
+  if (W >= 16) step(std::integral_constant<int, 0x140>()); // row_mirror
+}
+
 template <int W>
 __device__ __forceinline__ uint64_t seg_max(uint64_t v) {
+  if (W <= 16) {
+    seg_dpp_steps<W>([&](auto c) {
+      constexpr int C = decltype(c)::value;
+      const uint64_t o = ((uint64_t)dpp<C>((uint32_t)(v >> 32)) << 32) | dpp<C>((uint32_t)v);
+      v = o > v ? o : v;
+    });
+  } else {
 #pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, W);
-    v = w > v ? w : v;
+    for (int o = W / 2; o > 0; o >>= 1) {
+      uint64_t w = __shfl_xor(v, o, W);
+      v = w > v ? w : v;
+    }
   }
   return v;
 }
 
 template <int W>
 __device__ __forceinline__ float seg_sum(float v) {
+  if (W <= 16) {
+    seg_dpp_steps<W>([&](auto c) {
+      constexpr int C = decltype(c)::value;
+      v += __uint_as_float(dpp<C>(__float_as_uint(v)));
+    });
+  } else {
 #pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
+  }
   return v;
 }
 
@@ -184,9 +286,9 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   bool bad = false;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    int e = sl + i * W;
-    bool ok = act && e < E;
-    float x = ok ? row[e] : 0.0f;
+    const int e = sl + i * W;
+    const bool ok = act && e < E;
+    const float x = ok ? row[e] : 0.0f;
     val[i] = x;
     bad |= ok && !isfinite(x);
     key[i] = ok ? (((uint64_t)score_bits(x) << 32) | (uint32_t)(~(uint32_t)e)) : 0ull;
@@ -194,41 +296,44 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flags, MOE_FLAG_NONFINITE_LOGIT);
 
   uint32_t taken = 0;
-  uint64_t mine = 0;  // lane r < k keeps the key of the r-th winner
+  uint64_t mine = 0;   // lane r < k keeps the key of the r-th winner
+  uint64_t first = 0;  // every lane: the top key
   for (int r = 0; r < k; ++r) {
     uint64_t best = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i)
       if (!(taken & (1u << i)) && key[i] > best) best = key[i];
-    uint64_t win = seg_max<W>(best);
+    const uint64_t win = seg_max<W>(best);
 #pragma unroll
     for (int i = 0; i < V; ++i)
       if (key[i] == win && win != 0ull) taken |= 1u << i;
+    if (r == 0) first = win;
     if (sl == r) mine = win;
   }
 
   const bool holder = act && sl < k;
   const int my_id = (int)(~(uint32_t)(mine & 0xffffffffu));
-  const float my_v = holder ? row[my_id] : 0.0f;
+  // winners' scores come back from their keys (a NaN winner re-reads its score)
+  const uint32_t mb = (uint32_t)(mine >> 32), fb = (uint32_t)(first >> 32);
+  const float my_v = holder ? (mb == 1u ? row[my_id] : bits_score(mb)) : 0.0f;
+  const float top = fb == 1u ? __int_as_float(0x7fc00000) : bits_score(fb);
   float g = 0.f;
   if (mode == MOE_GATE_SOFTMAX) {
-    float mx = __shfl(my_v, 0, W);  // the first winner holds the largest number
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      int e = sl + i * W;
-      if (act && e < E) part += __expf(val[i] - mx);
+      const int e = sl + i * W;
+      if (act && e < E) part += __expf(val[i] - top);
     }
-    float sum = seg_sum<W>(part);
-    g = __expf(my_v - mx) / sum;
+    const float sum = seg_sum<W>(part);
+    g = __expf(my_v - top) / sum;
   } else if (mode == MOE_GATE_SOFTMAX_TOPK_RENORM) {
-    float top = __shfl(my_v, 0, W);
-    float ex = holder ? __expf(my_v - top) : 0.f;
-    float sum = seg_sum<W>(ex);
+    const float ex = holder ? __expf(my_v - top) : 0.f;
+    const float sum = seg_sum<W>(ex);
     g = ex / sum;
   } else {
-    float sg = holder ? 1.0f / (1.0f + __expf(-my_v)) : 0.f;
-    float sum = seg_sum<W>(sg);
+    const float sg = holder ? 1.0f / (1.0f + __expf(-my_v)) : 0.f;
+    const float sum = seg_sum<W>(sg);
     g = sg / sum;
   }
   if (holder) {
@@ -254,10 +359,10 @@ hipError_t launch_topk(const float* logits, int32_t* idx, float* gate, uint32_t*
   if (E <= 4) return topk_launch<4, 1>(logits, idx, gate, flags, T, E, k, mode, s);
   if (E <= 8) return topk_launch<8, 1>(logits, idx, gate, flags, T, E, k, mode, s);
   if (E <= 16) return topk_launch<16, 1>(logits, idx, gate, flags, T, E, k, mode, s);
-  if (E <= 32) return topk_launch<32, 1>(logits, idx, gate, flags, T, E, k, mode, s);
-  if (E <= 64) return topk_launch<64, 1>(logits, idx, gate, flags, T, E, k, mode, s);
-  if (E <= 128) return topk_launch<64, 2>(logits, idx, gate, flags, T, E, k, mode, s);
-  if (E <= 256) return topk_launch<64, 4>(logits, idx, gate, flags, T, E, k, mode, s);
+  if (E <= 32) return topk_launch<16, 2>(logits, idx, gate, flags, T, E, k, mode, s);
+  if (E <= 64) return topk_launch<16, 4>(logits, idx, gate, flags, T, E, k, mode, s);
+  if (E <= 128) return topk_launch<16, 8>(logits, idx, gate, flags, T, E, k, mode, s);
+  if (E <= 256) return topk_launch<16, 16>(logits, idx, gate, flags, T, E, k, mode, s);
   if (E <= 512) return topk_launch<64, 8>(logits, idx, gate, flags, T, E, k, mode, s);
   return topk_launch<64, 16>(logits, idx, gate, flags, T, E, k, mode, s);
 }

@@ -159,3 +159,16 @@ def test_all_tokens_to_one_expert_large():
         ref = check_plan(G, desc, idx, bufs, E, cap, T * k)
         _check_rows(bufs, h, ref)
         say(f"one-hot expert cap={cap} counts[0]={host(bufs.counts)[0]}")
+
+
+@pytest.mark.parametrize("cap", [-1, 30])
+def test_large_plan_takes_the_separate_scan_path(cap):
+    """157 tiles x 1024 experts exceeds the plan size the rank kernel scans by
+    itself, so the standalone scan kernel runs; results must not change."""
+    G = lib()
+    T, E, k = 20000, 1024, 2
+    rng = np.random.default_rng(21)
+    idx = _skewed_routes(rng, T, E, k)
+    desc, bufs, h = _permute(G, idx, E, capacity=cap, d=64)
+    ref = check_plan(G, desc, idx, bufs, E, cap, T * k)
+    _check_rows(bufs, h, ref)
