@@ -1,6 +1,7 @@
 // C ABI entry points: argument validation on the host, then kernel launches
 // enqueued on the caller's stream. Nothing here synchronises, copies device
 // data to the host or allocates memory.
+#include <algorithm>
 #include "common.h"
 
 #define MOE_EXPORT extern "C" __attribute__((visibility("default")))
@@ -43,7 +44,14 @@ static moe_status_t check_desc(const moe_layer_desc_t* d) {
   if (d->ep_rank < 0 || d->ep_rank >= d->ep_size) return MOE_ERR_SHAPE;
   if (d->max_rows < 0 || d->max_rows >= (int64_t)1 << 31) return MOE_ERR_SHAPE;
   if (d->T * (int64_t)d->k >= (int64_t)1 << 31) return MOE_ERR_SHAPE;
-  if (d->dtype == MOE_DTYPE_BF16 && (d->d % 64 != 0 || d->d_ff % 64 != 0)) return MOE_ERR_SHAPE;
+  if (d->dtype == MOE_DTYPE_BF16) {
+    if (d->d % 64 != 0 || d->d_ff % 64 != 0) return MOE_ERR_SHAPE;
+    // the expert GEMMs address one tile's operands with 32-bit byte offsets:
+    // gate and up weight rows of one expert, and 512 rows of either width
+    const int64_t lim = (int64_t)1 << 32;
+    if ((2 * (int64_t)d->d_ff + 256) * d->d * 2 >= lim) return MOE_ERR_SHAPE;
+    if ((int64_t)512 * std::max(d->d, d->d_ff) * 2 >= lim) return MOE_ERR_SHAPE;
+  }
   return MOE_OK;
 }
 

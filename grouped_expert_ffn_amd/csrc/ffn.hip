@@ -47,27 +47,91 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int EPI, int BK, int STAGES, int GROUP_M, int MF>
+// Tiles that do not fill a whole round of the persistent grid: when they
+// would occupy at most half of it, the main kernel stops after the whole
+// rounds and a second launch runs each leftover tile as two half-height
+// tiles, which keeps more CUs busy. Splitting by rows leaves every output's
+// K accumulation order unchanged, so results do not depend on the split.
+__device__ __forceinline__ int main_tile_end(int total, int G) {
+  const int full = total / G * G;
+  const int tail = total - full;
+  return (tail > 0 && 2 * tail <= G) ? full : total;
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ W, bf16* __restrict__ C,
     const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr, int N, int K,
     int64_t w_stride, int n_n, int64_t ldc) {
-  using TG = TileGemmDL<BM, BN, WM, WN, EPI, BK, STAGES, MF>;
+  using TG = TileGemmDL<BM, BN, WM, WN, EPI, BK, MF>;
+  __shared__ __attribute__((aligned(1024))) bf16 lds[TG::LDS_ELEMS];
+  const int n_m = *n_mt_ptr;
+  const int G = gridDim.x;
+  const int end = main_tile_end(n_m * n_n, G);
+  const int nk = K / BK;
+  // this workgroup's i-th tile, in XCD-major, GROUP_M-grouped order
+  auto get = [&](int i, GemmTile& t) -> bool {
+    const int v = xcd_virtual_id(blockIdx.x, G, i);
+    if (v >= end) return false;
+    int mt, nt;
+    tile_coords<GROUP_M>(v, n_m, n_n, mt, nt);
+    const int4 e = tiles[mt];   // expert, first row, end row
+    // the entry is the same for the whole workgroup: keep it in scalar registers
+    const int ex = __builtin_amdgcn_readfirstlane(e.x);
+    const int ey = __builtin_amdgcn_readfirstlane(e.y);
+    const int ez = __builtin_amdgcn_readfirstlane(e.z);
+    t.a = A + (int64_t)ey * K;
+    t.a_rows = ez - ey;
+    t.n0 = nt * BN;
+    t.b = W + (int64_t)ex * w_stride + (int64_t)t.n0 * K;
+    t.c_row = ey;
+    t.nk = nk;
+    return true;
+  };
+  TG::run_tiles(get, N, K, C, ldc, lds);
+}
+
+// The leftover tiles of the kernel above (same tile table, same order), as
+// half-height tiles of HM = BM / 2 rows: unit u is half u & 1 of tile
+// main_tile_end + u / 2. G is the main kernel's grid size.
+template <int HM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF>
+__global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ W, bf16* __restrict__ C,
+    const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr, int N, int K,
+    int64_t w_stride, int n_n, int64_t ldc, int G) {
+  using TG = TileGemmDL<HM, BN, WM, WN, EPI, BK, MF>;
   __shared__ __attribute__((aligned(1024))) bf16 lds[TG::LDS_ELEMS];
   const int n_m = *n_mt_ptr;
   const int total = n_m * n_n;
-  const int G = gridDim.x;
-  for (int it = 0; it * G < total; ++it) {
-    const int v = xcd_virtual_id(blockIdx.x, G, it);
-    if (v >= total) continue;
-    int mt, nt;
-    tile_coords<GROUP_M>(v, n_m, n_n, mt, nt);
-    const int4 t = tiles[mt];
-    TG::run(A, t.y, t.z - t.y, W + (int64_t)t.x * w_stride, nt * BN, N, K, C, ldc, lds);
-  }
+  const int first = main_tile_end(total, G);
+  const int units = 2 * (total - first);
+  const int nk = K / BK;
+  const int slot = xcd_virtual_id(blockIdx.x, gridDim.x, 0);
+  auto get = [&](int i, GemmTile& t) -> bool {
+    // one unit per workgroup at most (units <= G); an empty lower half
+    // (a tile of HM rows or fewer) is skipped
+    for (int u = slot + i * (int)gridDim.x; u < units; u += gridDim.x) {
+      int mt, nt;
+      tile_coords<GROUP_M>(first + u / 2, n_m, n_n, mt, nt);
+      const int4 e = tiles[mt];
+      const int ex = __builtin_amdgcn_readfirstlane(e.x);
+      const int ey = __builtin_amdgcn_readfirstlane(e.y) + (u & 1) * HM;
+      const int ez = __builtin_amdgcn_readfirstlane(e.z);
+      if (ey >= ez) continue;
+      t.a = A + (int64_t)ey * K;
+      t.a_rows = min(ez - ey, HM);
+      t.n0 = nt * BN;
+      t.b = W + (int64_t)ex * w_stride + (int64_t)t.n0 * K;
+      t.c_row = ey;
+      t.nk = nk;
+      return true;
+    }
+    return false;
+  };
+  TG::run_tiles(get, N, K, C, ldc, lds);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int BK, int STAGES, int GROUP_M, int MF>
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF>
 static hipError_t grouped_gemm_dl_launch(const bf16* A, const bf16* W, bf16* C,
                                          const int4* tiles, const int* n_mt, int N, int K,
                                          int64_t w_stride, int64_t ldc, int64_t max_mtiles,
@@ -76,8 +140,13 @@ static hipError_t grouped_gemm_dl_launch(const bf16* A, const bf16* W, bf16* C,
   const int64_t ub = max_mtiles * n_n;
   int64_t G = min(((ub + 7) / 8) * 8, (int64_t)device_cu_count() * per_cu);
   G = max((int64_t)8, G / 8 * 8);
-  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BN, WM, WN, EPI, BK, STAGES, GROUP_M, MF>), dim3((unsigned)G),
+  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BN, WM, WN, EPI, BK, GROUP_M, MF>), dim3((unsigned)G),
                      dim3(64 * WM * WN), 0, s, A, W, C, tiles, n_mt, N, K, w_stride, n_n, ldc);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((grouped_gemm_tail_kernel<BM / 2, BN, WM, WN, EPI, BK, GROUP_M, MF>),
+                     dim3((unsigned)G), dim3(64 * WM * WN), 0, s, A, W, C, tiles, n_mt, N, K,
+                     w_stride, n_n, ldc, (int)G);
   return hipGetLastError();
 }
 
@@ -183,13 +252,13 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
     const bf16* X = (const bf16*)x_perm;
     bf16* H = (bf16*)act;
     if (swiglu)
-      err = grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_SWIGLU_BF16, 64, 2, kGemmGroupM, 16>(
+      err = grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_SWIGLU_BF16, 64, kGemmGroupM, 16>(
           X, (const bf16*)w1, H, tiles, n_mt, dff, d, (int64_t)w1_rows * d, dff, mt_ub, 1, s);
     else
-      err = grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_RELU_BF16, 64, 2, kGemmGroupM, 16>(
+      err = grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_RELU_BF16, 64, kGemmGroupM, 16>(
           X, (const bf16*)w1, H, tiles, n_mt, dff, d, (int64_t)w1_rows * d, dff, mt_ub, 1, s);
     if (err != hipSuccess) return err;
-    return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_STORE_BF16, 64, 2, kGemmGroupM, 16>(
+    return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_STORE_BF16, 64, kGemmGroupM, 16>(
         H, (const bf16*)w2, (bf16*)y_perm, tiles, n_mt, d, dff, (int64_t)d * dff, d, mt_ub, 1, s);
   }
   hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,

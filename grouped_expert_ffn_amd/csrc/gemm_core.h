@@ -22,13 +22,16 @@ namespace moe {
 
 enum Epilogue { EPI_STORE_BF16 = 0, EPI_SWIGLU_BF16 = 1, EPI_ROUTER_F32 = 2, EPI_RELU_BF16 = 3 };
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+// SiLU with the hardware reciprocal (about 1 ulp): g * 1 / (1 + e^-g)
+__device__ __forceinline__ float silu_f(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
 
 // ---------------------------------------------------------------------------
 // The tile: K slices of A and B go from global memory straight into LDS
 // (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16 *
-// lane), so no VGPRs or ds_write instructions are spent on staging; STAGES
-// slices are kept in flight (STAGES-1 ahead of the one being multiplied).
+// lane), so no VGPRs or ds_write instructions are spent on staging; two
+// slices are kept in LDS, the next one in flight while one is multiplied.
 // One such load fills 1 KiB of consecutive LDS rows; the XOR swizzle of the
 // 16-byte chunks is kept by choosing which global chunk each lane fetches.
 template <int BK>
@@ -44,8 +47,12 @@ struct SliceLayout {
 // drain outstanding global loads, so slices prefetched into LDS by
 // global_load_lds stay in flight across it (their completion is awaited
 // explicitly with wait_vmcnt before the barrier that publishes them).
+// The lgkmcnt wait goes through the builtin so the compiler's own wait
+// insertion knows that every earlier LDS read has returned; the barrier itself
+// is an asm statement with a memory clobber, so no LDS access moves across it.
 __device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt: no wait
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // s_waitcnt with vmcnt <= N and no wait on the other counters (gfx9 encoding).
@@ -55,7 +62,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int BK = 64, int STAGES = 2, int MF = 16>
+// One output tile as the persistent loop sees it.
+struct GemmTile {
+  const bf16* a;    // first A row of the tile (row stride K)
+  const bf16* b;    // weight row n0 (row stride K); with the gated epilogue the
+                    // matching up-projection rows sit N rows further on
+  int a_rows;       // valid A rows, 1..BM (rows past them are not stored)
+  int n0;           // first output column
+  int64_t c_row;    // output row of the tile's first A row
+  int nk;           // K slices (of BK) to multiply
+};
+
+// Persistent tile loop of one workgroup: run_tiles(get, ...) multiplies the
+// tiles get(0), get(1), ... until get returns false. K slices stream through
+// two LDS buffers as one sequence that runs across tile boundaries: the next
+// tile's first slices are already in flight while the current tile's
+// epilogue converts and stores its accumulators.
+template <int BM, int BN, int WM, int WN, int EPI, int BK = 64, int MF = 16>
 struct TileGemmDL {
   using L = SliceLayout<BK>;
   static constexpr int NT = 64 * WM * WN;
@@ -68,80 +91,116 @@ struct TileGemmDL {
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int TM = WTM / MF, TN = WTN / MF;   // MFMA tiles per wave
   static constexpr int LDS_BUF = ROWS * BK;
-  static constexpr int LDS_ELEMS = STAGES * LDS_BUF;
+  static constexpr int LDS_ELEMS = 2 * LDS_BUF;
   using Acc = typename std::conditional<MF == 32, f32x16, f32x4>::type;
   static constexpr int NACC = MF == 32 ? 16 : 4;
+  static constexpr int KSUB = MF == 32 ? 16 : 32;  // K per MFMA
+  static constexpr int CPS = KSUB / 8;             // 16-byte chunks per sub-step
+  static constexpr int NSUB = BK / KSUB;           // sub-steps per slice
+  static constexpr int TU = GATED ? TN : 1;
   static_assert(MF == 16 || MF == 32, "MFMA shape");
   static_assert(LOADS % NW == 0, "loads must split evenly over waves");
   static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be a multiple of the MFMA tile");
-  static_assert(BK % 32 == 0 && STAGES >= 2, "K slice and stage count");
-  static_assert((STAGES - 2) * LPW < 64, "vmcnt range");
+  static_assert(BK % 32 == 0 && NSUB >= 2, "two or more MFMA sub-steps per K slice");
+  static_assert(BM % L::RPL == 0, "a load must not straddle the A and B rows");
 
   // C is bf16 (row stride ldc) for the expert epilogues; for EPI_ROUTER_F32 it
   // is float, bias (or null) is added and only columns < n_store are written.
-  __device__ __forceinline__ static void run(const bf16* __restrict__ A, int64_t a0, int a_rows,
-                                             const bf16* __restrict__ B, int n0, int N, int K,
-                                             void* __restrict__ Cv, int64_t ldc, bf16* lds,
-                                             const float* __restrict__ bias = nullptr,
-                                             int n_store = 0) {
+  // N is the weight's output width (rows past it are clamped onto row N-1 and
+  // their columns not stored); K is the operands' row stride, every tile has
+  // nk >= 1 slices of BK, and every operand byte a tile reads must lie within
+  // 4 GiB of its a / b pointer.
+  template <class GetTile>
+  __device__ __forceinline__ static void run_tiles(GetTile get, int N, int K,
+                                                   void* __restrict__ Cv, int64_t ldc, bf16* lds,
+                                                   const float* __restrict__ bias = nullptr,
+                                                   int n_store = 0) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wm = wave / WN;
     const int wn = wave % WN;
 
-    // per-lane element offset of each of this wave's loads, relative to the
-    // tile's first A row (loads into A rows) or first weight row (B rows);
-    // rows past the end are clamped onto the last valid row
-    const bf16* Ab = A + a0 * (int64_t)K;
-    const bf16* Bb = B + (int64_t)n0 * K;
-    uint32_t off[LPW];
+    // ---- global -> LDS loads. Load i of this wave fills LDS rows
+    // (wave * LPW + i) * RPL .. + RPL - 1 of a slice; whether those are A or
+    // weight rows is uniform across the wave (RPL divides BM).
     bool is_a[LPW];
+    uint32_t off[LPW];   // per-lane byte offset from the tile's a / b pointer
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int r = (wave * LPW + i) * L::RPL + lane / L::CPR;  // LDS row
-      const int c = L::swz(r, lane % L::CPR);                   // global chunk kept in that slot
-      is_a[i] = r < BM;
-      int row;
-      if (r < BM) {
-        row = r < a_rows ? r : a_rows - 1;
-      } else {
-        const int q = r - BM;
-        const int ql = (GATED && q >= BN) ? q - BN : q;
-        const int nn = n0 + ql < N ? ql : N - 1 - n0;
-        row = (GATED && q >= BN) ? N + nn : nn;
+    for (int i = 0; i < LPW; ++i) is_a[i] = (wave * LPW + i) * L::RPL < BM;
+    auto set_offsets = [&](const GemmTile& t) {
+      // the lane id is re-read here (volatile, so it stays inside the tile
+      // loop); otherwise the compiler keeps every load's row and chunk live
+      // across the loop for the next call, which costs 16 VGPRs
+      int ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int r = (wave * LPW + i) * L::RPL + ln / L::CPR;  // LDS row
+        const int c = L::swz(r, ln % L::CPR);                   // global chunk kept in that slot
+        int row;
+        if (is_a[i]) {
+          row = r < t.a_rows ? r : t.a_rows - 1;
+        } else {
+          const int q = r - BM;
+          const int ql = (GATED && q >= BN) ? q - BN : q;
+          const int nn = t.n0 + ql < N ? ql : N - 1 - t.n0;
+          row = (GATED && q >= BN) ? N + nn : nn;
+        }
+        off[i] = ((uint32_t)row * (uint32_t)K + (uint32_t)(c * 8)) * 2u;
       }
-      off[i] = (uint32_t)row * (uint32_t)K + (uint32_t)(c * 8);
-    }
-
-    Acc acc[TN][TM];
-    Acc acc2[GATED ? TN : 1][GATED ? TM : 1];
-#pragma unroll
-    for (int x = 0; x < TN; ++x)
-#pragma unroll
-      for (int y = 0; y < TM; ++y)
-#pragma unroll
-        for (int q = 0; q < NACC; ++q) acc[x][y][q] = 0.f;
-    if (GATED) {
-#pragma unroll
-      for (int x = 0; x < (GATED ? TN : 1); ++x)
-#pragma unroll
-        for (int y = 0; y < (GATED ? TM : 1); ++y)
-#pragma unroll
-          for (int q = 0; q < NACC; ++q) acc2[x][y][q] = 0.f;
-    }
-
-    auto issue = [&](int kt, int buf) {
+    };
+    // a scalar base plus a 32-bit per-lane byte offset: the load's saddr form,
+    // one VGPR per load instead of a 64-bit address
+    auto issue = [&](const GemmTile& t, int kt, int buf) {
       bf16* base = lds + buf * LDS_BUF + wave * LPW * L::RPL * BK;
-      const int ko = kt * BK;
+      const uint32_t ko = (uint32_t)kt * (BK * 2);
 #pragma unroll
-      for (int i = 0; i < LPW; ++i)
-        __builtin_amdgcn_global_load_lds((is_a[i] ? Ab : Bb) + (off[i] + ko),
-                                         base + i * L::RPL * BK, 16, 0, 0);
+      for (int i = 0; i < LPW; ++i) {
+        const char* src = reinterpret_cast<const char*>(is_a[i] ? t.a : t.b) + (off[i] + ko);
+        __builtin_amdgcn_global_load_lds(src, base + i * L::RPL * BK, 16, 0, 0);
+      }
+    };
+    // load cursor: the tile and slice fetched next
+    GemmTile lt;
+    int l_idx = 0, l_k = 0, tiles_end = 0x7fffffff;
+    bool l_live = get(0, lt);
+    if (!l_live) return;
+    GemmTile ct = lt;   // tile being multiplied
+    set_offsets(lt);
+    auto issue_next = [&](int buf) {
+      if (!l_live) return;
+      issue(lt, l_k, buf);
+      if (++l_k == lt.nk) {
+        l_k = 0;
+        l_live = get(++l_idx, lt);
+        if (l_live)
+          set_offsets(lt);
+        else
+          tiles_end = l_idx;
+      }
     };
 
-    // MFMA operand lanes: lane feeds row (lane % MF) and the 8 K values of
-    // 16-byte chunk (lane / MF) of the current K sub-step
+    // ---- MFMA side. Lane feeds row (lane % MF) and the 8 K values of
+    // 16-byte chunk (lane / MF) of the current K sub-step.
+    Acc acc[TN][TM];
+    Acc acc2[TU][GATED ? TM : 1];
+    auto zero_acc = [&]() {
+#pragma unroll
+      for (int x = 0; x < TN; ++x)
+#pragma unroll
+        for (int y = 0; y < TM; ++y)
+#pragma unroll
+          for (int q = 0; q < NACC; ++q) acc[x][y][q] = 0.f;
+      if (GATED) {
+#pragma unroll
+        for (int x = 0; x < TU; ++x)
+#pragma unroll
+          for (int y = 0; y < (GATED ? TM : 1); ++y)
+#pragma unroll
+            for (int q = 0; q < NACC; ++q) acc2[x][y][q] = 0.f;
+      }
+    };
     const int lr = lane % MF;
     const int lq = lane / MF;
     auto mma = [&](const bf16x8& w, const bf16x8& x, Acc& c) {
@@ -150,98 +209,154 @@ struct TileGemmDL {
       else
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, x, c, 0, 0, 0);
     };
-    constexpr int KSUB = MF == 32 ? 16 : 32;       // K per MFMA
-    constexpr int CPS = KSUB / 8;                  // 16-byte chunks per sub-step
-    auto compute = [&](int buf) {
+    // Operand fragments. The weight fragments of one K sub-step (TN, plus TU
+    // up-projection ones) are double-buffered; the TM token-row fragments are
+    // not: each is re-read for the next sub-step right after the last MFMA
+    // that uses it, into the same registers.
+    struct FragsB {
+      bf16x8 w[TN], u[TU];
+    };
+    bf16x8 fy[TM];
+    auto read_a = [&](int buf, int ks, int y) -> bf16x8 {
       const bf16* As = lds + buf * LDS_BUF;
-      const bf16* Bs = As + BM * BK;
+      const int ci = ks * CPS + lq;
+      const int r = wm * WTM + y * MF + lr;
+      return *reinterpret_cast<const bf16x8*>(As + r * BK + L::swz(r, ci) * 8);
+    };
+    auto read_b = [&](int buf, int ks, FragsB& f) {
+      const bf16* Bs = lds + buf * LDS_BUF + BM * BK;
+      const int ci = ks * CPS + lq;
 #pragma unroll
-      for (int ks = 0; ks < BK / KSUB; ++ks) {
-        const int ci = ks * CPS + lq;
-        bf16x8 yf[TM];
-#pragma unroll
-        for (int y = 0; y < TM; ++y) {
-          const int r = wm * WTM + y * MF + lr;
-          yf[y] = *reinterpret_cast<const bf16x8*>(As + r * BK + L::swz(r, ci) * 8);
+      for (int x = 0; x < TN; ++x) {
+        const int r = wn * WTN + x * MF + lr;
+        f.w[x] = *reinterpret_cast<const bf16x8*>(Bs + r * BK + L::swz(r, ci) * 8);
+        if (GATED) {
+          const int r2 = BN + r;
+          f.u[GATED ? x : 0] = *reinterpret_cast<const bf16x8*>(Bs + r2 * BK + L::swz(r2, ci) * 8);
         }
+      }
+    };
+    // multiply one sub-step (token fragments fy, weight fragments cur); with
+    // RD, read sub-step nks of buffer nbuf into fy and nxt meanwhile
+    auto step = [&](auto rd, const FragsB& cur, FragsB& nxt, int nbuf, int nks) {
+      constexpr bool RD = decltype(rd)::value;
+      if (RD) read_b(nbuf, nks, nxt);
+#pragma unroll
+      for (int y = 0; y < TM; ++y) {
 #pragma unroll
         for (int x = 0; x < TN; ++x) {
-          const int r = wn * WTN + x * MF + lr;
-          const bf16x8 wf = *reinterpret_cast<const bf16x8*>(Bs + r * BK + L::swz(r, ci) * 8);
+          mma(cur.w[x], fy[y], acc[x][y]);
+          if (GATED) mma(cur.u[GATED ? x : 0], fy[y], acc2[GATED ? x : 0][y]);
+        }
+        if (RD) fy[y] = read_a(nbuf, nks, y);
+      }
+      // issue order (sched_group_barrier masks: MFMA 0x008, DS read 0x100):
+      // the first token row's MFMAs each followed by one weight read, then
+      // every token row's MFMAs followed by that row's re-read
+      constexpr int NRB = TN + (GATED ? TU : 0);     // weight reads
+      constexpr int MPY = TN * (GATED ? 2 : 1);      // MFMAs per token row
+      if constexpr (RD && NRB == MPY) {
 #pragma unroll
-          for (int y = 0; y < TM; ++y) mma(wf, yf[y], acc[x][y]);
-          if (GATED) {
-            const int r2 = BN + r;
-            const bf16x8 wu = *reinterpret_cast<const bf16x8*>(Bs + r2 * BK + L::swz(r2, ci) * 8);
+        for (int i = 0; i < NRB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-            for (int y = 0; y < (GATED ? TM : 1); ++y) mma(wu, yf[y], acc2[(GATED ? x : 0)][y]);
+        for (int y = 1; y < TM; ++y) {
+          __builtin_amdgcn_sched_group_barrier(0x008, MPY, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+    };
+
+    // ---- epilogue: lane holds D[n][m = lr] for n = 8*g + 4*lq + i (32x32
+    // tiles, g = 0..3) or n = 4*lq + i (16x16 tiles), four consecutive
+    // columns at a time
+    auto epilogue = [&](const GemmTile& t) {
+#pragma unroll
+      for (int y = 0; y < TM; ++y) {
+        const int m = wm * WTM + y * MF + lr;
+        if (m >= t.a_rows) continue;
+#pragma unroll
+        for (int x = 0; x < TN; ++x) {
+#pragma unroll
+          for (int g = 0; g < NACC / 4; ++g) {
+            const int n = t.n0 + wn * WTN + x * MF + (MF == 32 ? 8 * g + 4 * lq : 4 * lq);
+            if constexpr (EPI == EPI_ROUTER_F32) {
+              float* out = reinterpret_cast<float*>(Cv) + (t.c_row + m) * ldc;
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (n + i < n_store) out[n + i] = acc[x][y][4 * g + i] + (bias ? bias[n + i] : 0.0f);
+            } else {
+              if (n >= N) continue;
+              bf16* out = reinterpret_cast<bf16*>(Cv) + (t.c_row + m) * ldc;
+              bf16x4 o;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                float v = acc[x][y][4 * g + i];
+                if (GATED) v = silu_f(v) * acc2[GATED ? x : 0][GATED ? y : 0][4 * g + i];
+                if (EPI == EPI_RELU_BF16) v = fmaxf(v, 0.0f);
+                o[i] = (bf16)v;
+              }
+              *reinterpret_cast<bf16x4*>(out + n) = o;
+            }
           }
         }
       }
     };
 
-    const int nk = K / BK;
-    if (STAGES == 2) {
-      // slice kt+1 streams into the other buffer while slice kt is multiplied;
-      // the closing barrier also frees the buffer just read for the next load
-      issue(0, 0);
-      wait_vmcnt<0>();
-      lds_barrier();
-      for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-        compute(kt & 1);
+    // ---- the tile and slice loops. Global slice g sits in LDS buffer g & 1.
+    // Fragment reads are software-pipelined across the slice barrier:
+    // sub-step 1 is read while sub-step 0 is multiplied, and sub-step 0 of
+    // slice g+1 is read right after the barrier that publishes it, while
+    // sub-step 1 of slice g is multiplied. Slice g+2 is fetched into the buffer slice g
+    // just left, so it has a whole slice of MFMAs to arrive. sched_barrier
+    // fences keep the compiler from moving MFMAs across the slice barrier,
+    // which would leave the reads before it uncovered.
+    static_assert(NSUB == 2, "the loop below pipelines two sub-steps per slice");
+    using Yes = std::integral_constant<bool, true>;
+    using No = std::integral_constant<bool, false>;
+    issue_next(0);
+    wait_vmcnt<0>();
+    lds_barrier();
+    issue_next(1);
+    FragsB b0, b1;
+    int g = 0;   // global slice index of this workgroup
+    for (int c_idx = 0;; ++c_idx) {
+      // the tile's first slice is in LDS buffer g & 1
+      zero_acc();
+      read_b(g & 1, 0, b0);
+#pragma unroll
+      for (int y = 0; y < TM; ++y) fy[y] = read_a(g & 1, 0, y);
+      for (int ck = 0; ck < ct.nk - 1; ++ck, ++g) {
+        const int buf = g & 1;
+        step(Yes{}, b0, b1, buf, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // slice g fully read by this wave; slice g+1 landed from this wave
         wait_vmcnt<0>();
         lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_next(buf);
+        step(Yes{}, b1, b0, buf ^ 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    } else {
-      // the previous tile's LDS reads and global stores are finished first
+      // the tile's last slice; its epilogue runs while the next tile's first
+      // slices load, and that tile's first fragments are read after it
+      const int buf = g & 1;
+      step(Yes{}, b0, b1, buf, 1);
+      __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<0>();
       lds_barrier();
-#pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) issue(s, s);
-      for (int kt = 0; kt < nk; ++kt) {
-        if (kt + STAGES - 1 <= nk)
-          wait_vmcnt<(STAGES - 2) * LPW>();
-        else
-          wait_vmcnt<0>();
-        lds_barrier();
-        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-        compute(kt % STAGES);
-      }
-    }
-
-    // epilogue: lane holds D[n][m = lr] for n = 8*g + 4*lq + i (32x32 tiles,
-    // g = 0..3) or n = 4*lq + i (16x16 tiles), four consecutive columns at a time
-#pragma unroll
-    for (int y = 0; y < TM; ++y) {
-      const int m = wm * WTM + y * MF + lr;
-      if (m >= a_rows) continue;
-#pragma unroll
-      for (int x = 0; x < TN; ++x) {
-#pragma unroll
-        for (int g = 0; g < NACC / 4; ++g) {
-          const int n = n0 + wn * WTN + x * MF + (MF == 32 ? 8 * g + 4 * lq : 4 * lq);
-          if constexpr (EPI == EPI_ROUTER_F32) {
-            float* out = reinterpret_cast<float*>(Cv) + (a0 + m) * ldc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (n + i < n_store) out[n + i] = acc[x][y][4 * g + i] + (bias ? bias[n + i] : 0.0f);
-          } else {
-            if (n >= N) continue;
-            bf16* out = reinterpret_cast<bf16*>(Cv) + (a0 + m) * ldc;
-            bf16x4 o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float v = acc[x][y][4 * g + i];
-              if (GATED) v = silu_f(v) * acc2[(GATED ? x : 0)][(GATED ? y : 0)][4 * g + i];
-              if (EPI == EPI_RELU_BF16) v = fmaxf(v, 0.0f);
-              o[i] = (bf16)v;
-            }
-            *reinterpret_cast<bf16x4*>(out + n) = o;
-          }
-        }
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      issue_next(buf);
+      step(No{}, b1, b0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      ++g;
+      epilogue(ct);
+      // the load cursor has already looked up the tile after this one
+      if (c_idx + 1 >= tiles_end) break;
+      get(c_idx + 1, ct);
     }
   }
 };

@@ -109,19 +109,25 @@ template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void router_tile_kernel(
     const bf16* __restrict__ h, const bf16* __restrict__ wt, const float* __restrict__ bias,
     float* __restrict__ logits, int64_t T, int d, int E, int E_pad, int n_m, int n_n) {
-  using TG = TileGemmDL<BM, BN, WM, WN, EPI_ROUTER_F32, 64, 2, 16>;
+  using TG = TileGemmDL<BM, BN, WM, WN, EPI_ROUTER_F32, 64, 16>;
   __shared__ __attribute__((aligned(1024))) bf16 lds[TG::LDS_ELEMS];
   const int total = n_m * n_n;
   const int G = gridDim.x;
-  for (int it = 0; it * G < total; ++it) {
-    const int v = xcd_virtual_id(blockIdx.x, G, it);
-    if (v >= total) continue;
+  auto get = [&](int i, GemmTile& t) -> bool {
+    const int v = xcd_virtual_id(blockIdx.x, G, i);
+    if (v >= total) return false;
     int mt, nt;
     tile_coords<8>(v, n_m, n_n, mt, nt);
     const int64_t a0 = (int64_t)mt * BM;
-    const int rows = (int)min((int64_t)BM, T - a0);
-    TG::run(h, a0, rows, wt, nt * BN, E_pad, d, logits, E, lds, bias, E);
-  }
+    t.a = h + a0 * d;
+    t.a_rows = (int)min((int64_t)BM, T - a0);
+    t.n0 = nt * BN;
+    t.b = wt + (int64_t)t.n0 * d;
+    t.c_row = a0;
+    t.nk = d / 64;
+    return true;
+  };
+  TG::run_tiles(get, E_pad, d, logits, E, lds, bias, E);
 }
 
 static int g_num_cu[64];

@@ -81,7 +81,8 @@ typedef struct moe_layer_desc {
   int32_t d;        /* hidden width (bf16: multiple of 64) */
   int32_t E;        /* experts, global count, 1..1024 */
   int32_t k;        /* experts per token, 1..min(E, 16) */
-  int32_t d_ff;     /* expert inner width (bf16: multiple of 64) */
+  int32_t d_ff;     /* expert inner width (bf16: multiple of 64, and
+                       (2 * d_ff + 256) * d * 2 bytes below 4 GiB) */
   int32_t dtype;    /* moe_dtype_t */
   int32_t gate;     /* moe_gate_t */
   int32_t act;      /* moe_act_t */

@@ -91,6 +91,15 @@ def test_null_and_alignment_and_workspace_errors(G):
     assert _call_route(G, desc, ws=300, ws_bytes=need) == 6   # not 256-aligned
 
 
+def test_bf16_weights_beyond_32bit_tile_offsets_rejected(G):
+    """The bf16 expert GEMMs address one expert's gate and up weight rows
+    with 32-bit byte offsets from the tile's weight pointer."""
+    ok = G.make_desc(64, 4096, 8, 2, 14336, "bf16", "softmax", "swiglu")
+    assert G.workspace_size(ok) > 0
+    too_wide = G.make_desc(64, 8192, 8, 2, 131072, "bf16", "softmax", "swiglu")
+    assert _call_route(G, too_wide) == 2
+
+
 def test_fp32_allows_any_width(G):
     desc = G.make_desc(64, 30, 4, 2, 50, "f32", "softmax", "relu")
     assert G.workspace_size(desc) > 0
