@@ -493,6 +493,74 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
   }
 }
 
+// The same combine for a compile-time k (1, 2, 4): all k rows' loads of a
+// chunk are issued before any of them is accumulated (k * U 16-byte loads in
+// flight per lane), then summed in slot order exactly as above. For larger k
+// the generic kernel already has enough rows in flight per wave.
+template <int KT, int U>
+__global__ __launch_bounds__(256) void combine_bf16_k_kernel(
+    const bf16x8* __restrict__ yp, const int32_t* __restrict__ idx,
+    const float* __restrict__ gate, const int32_t* __restrict__ dest, bf16x8* __restrict__ y,
+    int64_t T, int row_vec, int e_lo, int e_hi) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nw) {
+    int mine = -1;
+    float gm = 0.f;
+    if (lane < KT) {
+      int r = dest[t * KT + lane];
+      int e = idx[t * KT + lane];
+      if (r >= 0 && e >= e_lo && e < e_hi) {
+        mine = r;
+        gm = gate[t * KT + lane];
+      }
+    }
+    int rj[KT];
+    float gj[KT];
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      rj[j] = __builtin_amdgcn_readfirstlane(__shfl(mine, j));
+      gj[j] = __shfl(gm, j);
+    }
+    for (int c0 = lane; c0 < row_vec; c0 += 64 * U) {
+      bf16x8 v[KT][U];
+#pragma unroll
+      for (int j = 0; j < KT; ++j) {
+        if (rj[j] < 0) continue;
+        const bf16x8* src = yp + (int64_t)rj[j] * row_vec;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          int c = c0 + u * 64;
+          if (c < row_vec) v[j][u] = src[c];
+        }
+      }
+      float acc[U][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KT; ++j) {
+        if (rj[j] < 0) continue;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(gj[j], (float)v[j][u][i], acc[u][i]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int c = c0 + u * 64;
+        if (c < row_vec) {
+          bf16x8 o;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[i] = (bf16)acc[u][i];
+          __builtin_nontemporal_store(o, y + t * row_vec + c);
+        }
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void combine_f32_kernel(
     const float* __restrict__ yp, const int32_t* __restrict__ idx,
     const float* __restrict__ gate, const int32_t* __restrict__ dest, float* __restrict__ y,
@@ -518,9 +586,18 @@ hipError_t launch_combine(const void* y_perm, const int32_t* idx, const float* g
   if (T == 0) return hipSuccess;
   int64_t blocks = min((T + 3) / 4, (int64_t)device_cu_count() * 16);
   if (dtype == MOE_DTYPE_BF16) {
-    hipLaunchKernelGGL(combine_bf16_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       (const bf16x8*)y_perm, idx, gate, dest, (bf16x8*)y, T, k, d / 8, e_lo,
-                       e_hi);
+    const bf16x8* yp = (const bf16x8*)y_perm;
+    bf16x8* yo = (bf16x8*)y;
+    const int rv = d / 8;
+    const dim3 g((unsigned)blocks), b(256);
+    switch (k) {
+      case 1: hipLaunchKernelGGL((combine_bf16_k_kernel<1, 4>), g, b, 0, s, yp, idx, gate, dest, yo, T, rv, e_lo, e_hi); break;
+      case 2: hipLaunchKernelGGL((combine_bf16_k_kernel<2, 4>), g, b, 0, s, yp, idx, gate, dest, yo, T, rv, e_lo, e_hi); break;
+      case 4: hipLaunchKernelGGL((combine_bf16_k_kernel<4, 2>), g, b, 0, s, yp, idx, gate, dest, yo, T, rv, e_lo, e_hi); break;
+      default:
+        hipLaunchKernelGGL(combine_bf16_kernel<4>, g, b, 0, s, yp, idx, gate, dest, yo, T, k, rv,
+                           e_lo, e_hi);
+    }
   } else {
     hipLaunchKernelGGL(combine_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                        (const float*)y_perm, idx, gate, dest, (float*)y, T, k, d, e_lo, e_hi);
