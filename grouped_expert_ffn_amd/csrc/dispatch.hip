@@ -197,46 +197,12 @@ __global__ __launch_bounds__(64) void rank_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// 3'. Scan folded into the rank step, for plans up to kFusedPlanMax tile x
-//     expert counts: every workgroup (one per tile) reduces the tile
-//     histograms itself -- each expert's total and its prefix over earlier
-//     tiles, with LDS integer atomics -- so no separate scan launch is needed.
-//     Workgroup 0 also writes counts, offsets, splits and flags. The ranking
-//     then runs as in rank_kernel, on wave 0.
-constexpr int64_t kFusedPlanMax = 1 << 12;
-
-__global__ __launch_bounds__(256) void rank_scan_kernel(
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ tile_hist, int n_tiles,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ dest,
-    int32_t* __restrict__ src_token, int32_t* __restrict__ src_slot,
-    int64_t* __restrict__ send_splits, int64_t* __restrict__ send_displs, int ep_size,
-    uint32_t* __restrict__ flags, int64_t T, int E, int k, int ebits, int64_t capacity,
-    int64_t max_rows) {
-  __shared__ int32_t pre[kMaxE];       // prefix over earlier tiles, then the running position
-  __shared__ int32_t tot[kMaxE];       // per-expert totals
-  __shared__ int32_t off[kMaxE + 1];   // offsets
-  __shared__ int32_t wsum[256];
+// Exclusive scan over experts of min(total, capacity) by a 256-thread
+// workgroup: each thread takes a run of consecutive experts, then the 256 run
+// sums are scanned. Writes off[0..E]; returns whether any expert overflowed.
+__device__ bool scan_experts_block(const int32_t* tot, int32_t* off, int32_t* wsum, int E,
+                                   int64_t capacity) {
   const int tid = threadIdx.x;
-  const int tile = blockIdx.x;
-  for (int e = tid; e < E; e += 256) {
-    pre[e] = 0;
-    tot[e] = 0;
-  }
-  __syncthreads();
-  const int n = n_tiles * E;            // <= kFusedPlanMax
-#pragma unroll 8
-  for (int i = tid; i < n; i += 256) {
-    const int v = tile_hist[i];
-    if (v) {
-      const int t = i / E, e = i - t * E;
-      atomicAdd(&tot[e], v);
-      if (t < tile) atomicAdd(&pre[e], v);
-    }
-  }
-  __syncthreads();
-  // exclusive scan over experts of min(total, capacity): each thread takes a
-  // run of consecutive experts, then the 256 run sums are scanned
   const int per = (E + 255) / 256;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   int32_t local = 0;
@@ -262,7 +228,82 @@ __global__ __launch_bounds__(256) void rank_scan_kernel(
     run0 += (capacity >= 0 && (int64_t)c > capacity) ? (int32_t)capacity : c;
   }
   if (tid == 255) off[E] = wsum[255];
-  const bool any_drop = __syncthreads_or(drop);
+  return __syncthreads_or(drop);
+}
+
+// ---------------------------------------------------------------------------
+// 3'. Scan folded into the rank step, for plans up to kFusedPlanMax tile x
+//     expert counts: every workgroup (one per tile) reduces the tile
+//     histograms itself -- each expert's total and its prefix over earlier
+//     tiles, with LDS integer atomics -- so no separate scan launch is needed.
+//     Workgroup 0 also writes counts, offsets, splits and flags. The ranking
+//     then runs as in rank_kernel, on wave 0.
+constexpr int64_t kFusedPlanMax = 1 << 12;
+
+__global__ __launch_bounds__(256) void rank_scan_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ tile_hist, int n_tiles,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ dest,
+    int32_t* __restrict__ src_token, int32_t* __restrict__ src_slot,
+    int64_t* __restrict__ send_splits, int64_t* __restrict__ send_displs, int ep_size,
+    uint32_t* __restrict__ flags, int64_t T, int E, int k, int ebits, int64_t capacity,
+    int64_t max_rows) {
+  __shared__ int32_t pre[kMaxE];       // prefix over earlier tiles, then the running position
+  __shared__ int32_t tot[kMaxE];       // per-expert totals
+  __shared__ int32_t off[kMaxE + 1];   // offsets
+  __shared__ int32_t wsum[256];
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x;
+  // wave 0 fetches this tile's expert ids first, so their latency overlaps
+  // the histogram reduction and the scan
+  const int64_t a0 = (int64_t)tile * kTokTile * k;
+  const int64_t a1 = min(T * k, a0 + (int64_t)kTokTile * k);
+  constexpr int kMaxIt = kTokTile * kMaxK / 64;
+  int ids[kMaxIt];
+  if (tid < 64) {
+#pragma unroll
+    for (int it = 0; it < kMaxIt; ++it) {
+      const int64_t my = a0 + (int64_t)it * 64 + tid;
+      ids[it] = my < a1 ? idx[my] : -1;
+    }
+  }
+  for (int e = tid; e < E; e += 256) {
+    pre[e] = 0;
+    tot[e] = 0;
+  }
+  __syncthreads();
+  const int n = n_tiles * E;            // <= kFusedPlanMax
+#pragma unroll 8
+  for (int i = tid; i < n; i += 256) {
+    const int v = tile_hist[i];
+    if (v) {
+      const int t = i / E, e = i - t * E;
+      atomicAdd(&tot[e], v);
+      if (t < tile) atomicAdd(&pre[e], v);
+    }
+  }
+  __syncthreads();
+  // exclusive scan over experts of min(total, capacity)
+  bool any_drop;
+  if (E <= 64) {
+    // one wave, one expert per lane, shuffle scan: no workgroup barriers
+    if (tid < 64) {
+      const int32_t c = tid < E ? tot[tid] : 0;
+      const int32_t kp = (capacity >= 0 && (int64_t)c > capacity) ? (int32_t)capacity : c;
+      int32_t incl = kp;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int32_t up = __shfl_up(incl, o);
+        if (tid >= o) incl += up;
+      }
+      if (tid < E) off[tid] = incl - kp;
+      if (tid == E - 1) off[E] = incl;
+      wsum[0] = __any(kp < c);   // the same value from every lane of wave 0
+    }
+    __syncthreads();
+    any_drop = wsum[0] != 0;
+  } else {
+    any_drop = scan_experts_block(tot, off, wsum, E, capacity);
+  }
   if (tile == 0) {
     for (int e = tid; e < E; e += 256) {
       counts[e] = tot[e];
@@ -284,16 +325,7 @@ __global__ __launch_bounds__(256) void rank_scan_kernel(
   if (tid >= 64) return;
 
   const int lane = tid;
-  const int64_t a0 = (int64_t)tile * kTokTile * k;
-  const int64_t a1 = min(T * k, a0 + (int64_t)kTokTile * k);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  constexpr int kMaxIt = kTokTile * kMaxK / 64;
-  int ids[kMaxIt];
-#pragma unroll
-  for (int it = 0; it < kMaxIt; ++it) {
-    const int64_t my = a0 + (int64_t)it * 64 + lane;
-    ids[it] = my < a1 ? idx[my] : -1;
-  }
 #pragma unroll
   for (int it = 0; it < kMaxIt; ++it) {
     const int64_t a = a0 + (int64_t)it * 64;
