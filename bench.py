@@ -13,6 +13,11 @@ two MFMA GEMMs), per-stage figures, and the CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--skip-cpu-baseline]
+                    [--cold-steps N]
+
+After the timed steps, N more steps run one by one, each after a 512 MiB
+write that evicts the 256 MiB last-level cache (MALL); their event-timed
+median is reported as "cold_mall" beside (not in) the main figure.
 """
 from __future__ import annotations
 
@@ -41,11 +46,21 @@ def ffn_flops(n_rows, d, dff, act):
 FFN_SOURCES = ("common.h", "gemm_core.h", "ffn.hip")
 
 
-def kernel_source_sha():
-    """Hash of the sources the grouped-FFN kernels are built from."""
+def kernel_source_sha(names=FFN_SOURCES):
+    """Hash of the named kernel sources (default: those of the grouped FFN)."""
     h = hashlib.sha256()
-    for name in FFN_SOURCES:
+    for name in names:
         h.update(open(os.path.join(ROOT, "grouped_expert_ffn_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def library_sha():
+    """Hash of every HIP source of the library and its public header."""
+    csrc = os.path.join(ROOT, "grouped_expert_ffn_amd", "csrc")
+    h = hashlib.sha256(open(os.path.join(ROOT, "include", "moe_dispatch.h"), "rb").read())
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -100,6 +115,9 @@ def main():
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="extra steps, each after a 512 MiB write that evicts the 256 MiB MALL, "
+                         "timed one by one with events (reported beside the main figure)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -168,6 +186,25 @@ def main():
     wall = time.perf_counter() - t0
 
     stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])  # ms
+
+    # the same step with a cold last-level cache: a 512 MiB write before each
+    # step evicts the 256 MiB MALL (outside the events that time the step)
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+               for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            flush.fill_(i & 0xff)
+            step(cev[i])
+        torch.cuda.synchronize()
+        cst = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in cev])
+        cold = {"steps": args.cold_steps, "ms_per_step": float(np.median(cst.sum(axis=1))),
+                "route_ms": float(np.median(cst[:, 0])), "permute_ms": float(np.median(cst[:, 1])),
+                "grouped_ffn_ms": float(np.median(cst[:, 2])),
+                "combine_ms": float(np.median(cst[:, 3]))}
+        cold["tokens_per_s"] = cfg.T / (cold["ms_per_step"] / 1e3)
+        del flush
     st_ms = np.median(stage, axis=0)
     flags = int(b.flags.item())
     offs = b.offsets.cpu().numpy().astype(np.int64)
@@ -212,6 +249,9 @@ def main():
                 (permute_bytes + combine_bytes) / ((st_ms[1] + st_ms[3]) / 1e3) / 1e9 / HBM_PEAK_GBS,
             "rows_kept": n_kept, "rows_local": n_local, "flags": flags,
         },
+        "cold_mall": cold,
+        "env": {"device": torch.cuda.get_device_name(), "torch": torch.__version__,
+                "hip": torch.version.hip, "library_sha": library_sha()},
     }
     if not args.skip_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, capacity, args.cpu_sample_tokens,
