@@ -52,6 +52,18 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
 // rounds and a second launch runs each leftover tile as two half-height
 // tiles, which keeps more CUs busy. Splitting by rows leaves every output's
 // K accumulation order unchanged, so results do not depend on the split.
+// One tile-table entry, read with a vector load and made uniform again. A
+// scalar load would share the lgkm counter with the GEMM's LDS reads; with
+// both kinds pending the compiler can only wait for the counter to drain,
+// not for the oldest LDS reads.
+__device__ __forceinline__ int4 tile_entry(const int4* __restrict__ tiles, int mt) {
+  int mv;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(mv) : "s"(mt));
+  const int4 e = tiles[mv];
+  return make_int4(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
+                   __builtin_amdgcn_readfirstlane(e.z), 0);
+}
+
 __device__ __forceinline__ int main_tile_end(int total, int G) {
   const int full = total / G * G;
   const int tail = total - full;
@@ -75,11 +87,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
     if (v >= end) return false;
     int mt, nt;
     tile_coords<GROUP_M>(v, n_m, n_n, mt, nt);
-    const int4 e = tiles[mt];   // expert, first row, end row
-    // the entry is the same for the whole workgroup: keep it in scalar registers
-    const int ex = __builtin_amdgcn_readfirstlane(e.x);
-    const int ey = __builtin_amdgcn_readfirstlane(e.y);
-    const int ez = __builtin_amdgcn_readfirstlane(e.z);
+    const int4 e = tile_entry(tiles, mt);   // expert, first row, end row
+    const int ex = e.x, ey = e.y, ez = e.z;
     t.a = A + (int64_t)ey * K;
     t.a_rows = ez - ey;
     t.n0 = nt * BN;
@@ -113,10 +122,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
     for (int u = slot + i * (int)gridDim.x; u < units; u += gridDim.x) {
       int mt, nt;
       tile_coords<GROUP_M>(first + u / 2, n_m, n_n, mt, nt);
-      const int4 e = tiles[mt];
-      const int ex = __builtin_amdgcn_readfirstlane(e.x);
-      const int ey = __builtin_amdgcn_readfirstlane(e.y) + (u & 1) * HM;
-      const int ez = __builtin_amdgcn_readfirstlane(e.z);
+      const int4 e = tile_entry(tiles, mt);
+      const int ex = e.x, ey = e.y + (u & 1) * HM, ez = e.z;
       if (ey >= ez) continue;
       t.a = A + (int64_t)ey * K;
       t.a_rows = min(ez - ey, HM);

@@ -323,33 +323,36 @@ struct TileGemmDL {
     issue_next(1);
     FragsB b0, b1;
     int g = 0;   // global slice index of this workgroup
+    // The slice loop is rotated so that its head follows a slice barrier,
+    // where no LDS read is outstanding: the compiler's wait insertion is
+    // exact inside a loop body but waits for everything at a loop head that
+    // outstanding reads reach through the back edge.
     for (int c_idx = 0;; ++c_idx) {
       // the tile's first slice is in LDS buffer g & 1
       zero_acc();
       read_b(g & 1, 0, b0);
 #pragma unroll
       for (int y = 0; y < TM; ++y) fy[y] = read_a(g & 1, 0, y);
+      step(Yes{}, b0, b1, g & 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // slice g fully read by this wave; slice g+1 landed from this wave
+      wait_vmcnt<0>();
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
       for (int ck = 0; ck < ct.nk - 1; ++ck, ++g) {
         const int buf = g & 1;
-        step(Yes{}, b0, b1, buf, 1);
+        issue_next(buf);                       // slice g+2 into the buffer g left
+        step(Yes{}, b1, b0, buf ^ 1, 0);       // last sub-step of g, reads g+1
         __builtin_amdgcn_sched_barrier(0);
-        // slice g fully read by this wave; slice g+1 landed from this wave
-        wait_vmcnt<0>();
-        lds_barrier();
+        step(Yes{}, b0, b1, buf ^ 1, 1);       // sub-step 0 of g+1, reads its sub-step 1
         __builtin_amdgcn_sched_barrier(0);
-        issue_next(buf);
-        step(Yes{}, b1, b0, buf ^ 1, 0);
+        wait_vmcnt<0>();                       // slice g+2 landed from this wave ...
+        lds_barrier();                         // ... and slice g+1 read by every wave
         __builtin_amdgcn_sched_barrier(0);
       }
       // the tile's last slice; its epilogue runs while the next tile's first
       // slices load, and that tile's first fragments are read after it
-      const int buf = g & 1;
-      step(Yes{}, b0, b1, buf, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<0>();
-      lds_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      issue_next(buf);
+      issue_next(g & 1);
       step(No{}, b1, b0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       ++g;
