@@ -115,6 +115,9 @@ def main():
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
+    ap.add_argument("--gather", action="store_true",
+                    help="fused dispatch: permute makes only the plan and the first expert GEMM "
+                         "reads token rows from h through src_token")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps, each after a 512 MiB write that evicts the 256 MiB MALL, "
                          "timed one by one with events (reported beside the main figure)")
@@ -151,7 +154,8 @@ def main():
     h, wr = dev(inp["h"]), dev(inp["w_router"])
     bias = None if inp["bias"] is None else dev(inp["bias"], torch.float32)
     w1, w2 = dev(inp["w1"]), dev(inp["w2"])
-    b = G.alloc_buffers(desc)
+    gather = args.gather
+    b = G.alloc_buffers(desc, x_perm=not gather)
     ws = G.alloc_workspace(desc)
     y = torch.empty((cfg.T, cfg.d), dtype=dt, device="cuda")
     stream = torch.cuda.current_stream()
@@ -166,7 +170,10 @@ def main():
                   b.src_slot, b.send_splits, b.send_displs, b.flags, ws)
         if ev is not None:
             ev[2].record(stream)
-        G.grouped_ffn(desc, b.x_perm, b.offsets, w1, w2, b.y_perm, ws)
+        if gather:
+            G.grouped_ffn_gather(desc, h, b.src_token, b.offsets, w1, w2, b.y_perm, ws)
+        else:
+            G.grouped_ffn(desc, b.x_perm, b.offsets, w1, w2, b.y_perm, ws)
         if ev is not None:
             ev[3].record(stream)
         G.unpermute_combine(desc, b.y_perm, b.topk_idx, b.topk_gate, b.dest, y)
@@ -217,7 +224,7 @@ def main():
     # algorithmic bytes: permute reads each token row once and writes each kept
     # assignment's row, plus 12 B of ids/rows per assignment; combine reads the
     # local kept rows and writes one row per token, plus 12 B per assignment
-    permute_bytes = cfg.T * cfg.d * eb + n_kept * cfg.d * eb + 12 * Tk
+    permute_bytes = (0 if gather else cfg.T * cfg.d * eb + n_kept * cfg.d * eb) + 12 * Tk
     combine_bytes = n_local * cfg.d * eb + cfg.T * cfg.d * eb + 12 * Tk
     flops = ffn_flops(n_local, cfg.d, cfg.d_ff, cfg.act)
     ffn_s = st_ms[2] / 1e3
@@ -235,7 +242,9 @@ def main():
         "dtype": cfg.dtype, "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights)",
         "config": {"workload": f"{cfg.name}: {cfg.description}", "T": cfg.T, "d": cfg.d,
                    "E": cfg.E, "k": cfg.k, "d_ff": cfg.d_ff, "act": cfg.act, "gate": cfg.gate,
-                   "experts_local": el, "capacity": capacity, "parallelism": "1 GPU"},
+                   "experts_local": el, "capacity": capacity, "parallelism": "1 GPU",
+                   "dispatch": "rows gathered by the first expert GEMM" if gather
+                   else "rows copied into expert order"},
         "roofline": {"kernel": "grouped expert FFN (tile map + SwiGLU GEMM + down GEMM)",
                      "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,

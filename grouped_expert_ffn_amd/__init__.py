@@ -16,6 +16,7 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
+from typing import Optional
 
 import torch
 
@@ -29,7 +30,8 @@ FLAG_ROW_OVERFLOW, FLAG_BAD_EXPERT_ID, FLAG_NONFINITE_LOGIT, FLAG_DROPPED = 1, 2
 
 EXPORTED = ("moe_capacity_from_factor", "moe_workspace_size", "moe_route",
             "moe_topk_from_logits", "moe_permute", "moe_grouped_ffn",
-            "moe_unpermute_combine", "moe_layer_forward", "moe_status_str")
+            "moe_grouped_ffn_gather", "moe_unpermute_combine", "moe_layer_forward",
+            "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -55,7 +57,7 @@ class LayerBuffers(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m grouped_expert_ffn_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python grouped_expert_ffn_amd/build.py` "
             "(no CPU fallback exists)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
@@ -67,6 +69,7 @@ def _load():
         "moe_topk_from_logits": (I32, [D, P, P, P, P, P]),
         "moe_permute": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_grouped_ffn": (I32, [D, P, P, P, P, P, P, SZ, P]),
+        "moe_grouped_ffn_gather": (I32, [D, P, P, P, P, P, P, P, SZ, P]),
         "moe_unpermute_combine": (I32, [D, P, P, P, P, P, P]),
         "moe_layer_forward": (I32, [D, P, P, P, P, P, P, ctypes.POINTER(LayerBuffers), P, SZ, P]),
         "moe_status_str": (ctypes.c_char_p, [I32]),
@@ -164,12 +167,14 @@ class LayerBuffersT:
     src_slot: torch.Tensor
     send_splits: torch.Tensor
     send_displs: torch.Tensor
-    x_perm: torch.Tensor
+    x_perm: Optional[torch.Tensor]   # None: the fused call gathers rows from h
     y_perm: torch.Tensor
     flags: torch.Tensor
 
 
-def alloc_buffers(desc: LayerDesc, device="cuda") -> LayerBuffersT:
+def alloc_buffers(desc: LayerDesc, device="cuda", x_perm=True) -> LayerBuffersT:
+    """Every buffer of the fused call; with x_perm=False the expert-ordered
+    copy of the rows is left out (the first expert GEMM then gathers them)."""
     T, E, k, d, R = desc.T, desc.E, desc.k, desc.d, desc.max_rows
     dt = torch_dtype(desc)
     i32, f32 = torch.int32, torch.float32
@@ -184,7 +189,7 @@ def alloc_buffers(desc: LayerDesc, device="cuda") -> LayerBuffersT:
         src_slot=torch.full((max(R, 1),), -1, dtype=i32, device=device)[:R],
         send_splits=torch.empty((desc.ep_size,), dtype=torch.int64, device=device),
         send_displs=torch.empty((desc.ep_size,), dtype=torch.int64, device=device),
-        x_perm=torch.empty((R, d), dtype=dt, device=device),
+        x_perm=torch.empty((R, d), dtype=dt, device=device) if x_perm else None,
         y_perm=torch.empty((R, d), dtype=dt, device=device),
         flags=torch.zeros((1,), dtype=torch.int32, device=device),
     )
@@ -223,7 +228,8 @@ def permute(desc, h, topk_idx, x_perm, counts, offsets, dest, src_token, src_slo
     _check(_lib.moe_permute(
         ctypes.byref(desc), _ptr(h, "h", dt, (T, d)),
         _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
-        _ptr(x_perm, "x_perm", dt, (R, d)), _ptr(counts, "counts", torch.int32, (E,)),
+        _ptr(x_perm, "x_perm", dt, (R, d), optional=True),
+        _ptr(counts, "counts", torch.int32, (E,)),
         _ptr(offsets, "offsets", torch.int32, (E + 1,)),
         _ptr(dest, "dest", torch.int32, (T, k)),
         _ptr(src_token, "src_token", torch.int32, (R,)),
@@ -249,6 +255,19 @@ def grouped_ffn(desc, x_perm, offsets, w1, w2, y_perm, ws, stream=None):
         _ptr(offsets, "offsets", torch.int32, (desc.E + 1,)),
         _ptr(w1, "w1", dt, s1), _ptr(w2, "w2", dt, s2), _ptr(y_perm, "y_perm", dt, (R, d)),
         wsp, wsn, _stream(stream)), "moe_grouped_ffn")
+
+
+def grouped_ffn_gather(desc, h, src_token, offsets, w1, w2, y_perm, ws, stream=None):
+    dt = torch_dtype(desc)
+    s1, s2 = _w_shapes(desc)
+    T, R, d = desc.T, desc.max_rows, desc.d
+    wsp, wsn = _ws(ws)
+    _check(_lib.moe_grouped_ffn_gather(
+        ctypes.byref(desc), _ptr(h, "h", dt, (T, d)),
+        _ptr(src_token, "src_token", torch.int32, (R,)),
+        _ptr(offsets, "offsets", torch.int32, (desc.E + 1,)),
+        _ptr(w1, "w1", dt, s1), _ptr(w2, "w2", dt, s2), _ptr(y_perm, "y_perm", dt, (R, d)),
+        wsp, wsn, _stream(stream)), "moe_grouped_ffn_gather")
 
 
 def unpermute_combine(desc, y_perm, topk_idx, topk_gate, dest, y, stream=None):
@@ -277,7 +296,7 @@ def layer_forward(desc, h, w_router, bias, w1, w2, y, bufs: LayerBuffersT, ws, s
         src_slot=_ptr(bufs.src_slot, "src_slot", torch.int32, (R,)).value,
         send_splits=_ptr(bufs.send_splits, "send_splits", torch.int64, (desc.ep_size,)).value,
         send_displs=_ptr(bufs.send_displs, "send_displs", torch.int64, (desc.ep_size,)).value,
-        x_perm=_ptr(bufs.x_perm, "x_perm", dt, (R, d)).value,
+        x_perm=(None if bufs.x_perm is None else _ptr(bufs.x_perm, "x_perm", dt, (R, d)).value),
         y_perm=_ptr(bufs.y_perm, "y_perm", dt, (R, d)).value,
         flags=_ptr(bufs.flags, "flags", torch.int32, (1,)).value)
     wsp, wsn = _ws(ws)

@@ -1,4 +1,7 @@
-"""Build the HIP library (gfx950) in-tree: ``python -m grouped_expert_ffn_amd.build``.
+"""Build the HIP library (gfx950) in-tree: ``python grouped_expert_ffn_amd/build.py``.
+
+This file uses the standard library only, so it runs (and imports) without
+the package, whose import needs the library already built.
 
 Every ``csrc/*.hip`` file is compiled to an object in parallel under
 ``_build/``, then linked into ``libmoe_dispatch.so`` next to this file.

@@ -115,17 +115,28 @@ static moe_status_t do_permute(const moe_layer_desc_t& d, const void* h, const i
   HIP_TRY(launch_dispatch_plan(idx, tile_hist, counts, offsets, dest, src_token, src_slot, splits,
                                displs, flags, d.T, d.E, d.k, d.capacity, d.max_rows, d.ep_size,
                                s));
-  HIP_TRY(launch_permute_rows(h, dest, x_perm, d.T, d.k, (int)(d.d * elt_bytes(d.dtype)), s));
+  // without x_perm only the plan is made (the rows are gathered later)
+  if (x_perm)
+    HIP_TRY(launch_permute_rows(h, dest, x_perm, d.T, d.k, (int)(d.d * elt_bytes(d.dtype)), s));
   return MOE_OK;
 }
 
-static moe_status_t do_ffn(const moe_layer_desc_t& d, const void* x_perm, const int32_t* offsets,
-                           const void* w1, const void* w2, void* y_perm, char* ws,
-                           hipStream_t s) {
+// rows == null: x holds the expert-ordered rows (x_perm); otherwise x is h and
+// row i of the grouped operand is h[rows[i]]
+static moe_status_t do_ffn(const moe_layer_desc_t& d, const void* x, const int32_t* rows,
+                           const int32_t* offsets, const void* w1, const void* w2, void* y_perm,
+                           char* ws, hipStream_t s) {
   const Workspace w = workspace_layout(d);
   if (d.max_rows == 0) return MOE_OK;
-  HIP_TRY(launch_grouped_ffn(d, x_perm, offsets, w1, w2, y_perm, ws + w.act,
+  HIP_TRY(launch_grouped_ffn(d, x, rows, offsets, w1, w2, y_perm, ws + w.act,
                              reinterpret_cast<int4*>(ws + w.gemm_tiles), s));
+  return MOE_OK;
+}
+
+// gathered bf16 rows are addressed with 32-bit byte offsets from h
+static moe_status_t check_gather(const moe_layer_desc_t& d) {
+  if (d.dtype == MOE_DTYPE_BF16 && d.T * (int64_t)d.d * 2 >= ((int64_t)1 << 32))
+    return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -192,7 +203,8 @@ MOE_EXPORT moe_status_t moe_permute(const moe_layer_desc_t* desc, const void* h,
   MOE_TRY(check_desc(desc));
   const moe_layer_desc_t& d = *desc;
   const int64_t Tk = d.T * d.k, R = d.max_rows;
-  MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {x_perm, R * d.d, true}, {topk_idx, Tk, false},
+  MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {x_perm, x_perm ? R * d.d : 0, true},
+                            {topk_idx, Tk, false},
                             {counts, d.E, false}, {offsets, d.E + 1, false}, {dest, Tk, false},
                             {src_token, R, false}, {src_slot, R, false}, {flags, 1, false},
                             {send_splits, d.ep_size, false}, {send_displs, d.ep_size, false}}));
@@ -211,7 +223,23 @@ MOE_EXPORT moe_status_t moe_grouped_ffn(const moe_layer_desc_t* desc, const void
   MOE_TRY(check_bufs(desc, {{x_perm, R * d.d, true}, {y_perm, R * d.d, true}, {w1, w1n, true},
                             {w2, w2n, true}, {offsets, d.E + 1, false}}));
   MOE_TRY(check_ws(desc, ws, ws_bytes));
-  return do_ffn(*desc, x_perm, offsets, w1, w2, y_perm, (char*)ws, (hipStream_t)stream);
+  return do_ffn(*desc, x_perm, nullptr, offsets, w1, w2, y_perm, (char*)ws, (hipStream_t)stream);
+}
+
+MOE_EXPORT moe_status_t moe_grouped_ffn_gather(const moe_layer_desc_t* desc, const void* h,
+                                               const int32_t* src_token, const int32_t* offsets,
+                                               const void* w1, const void* w2, void* y_perm,
+                                               void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_layer_desc_t& d = *desc;
+  MOE_TRY(check_gather(d));
+  const int64_t R = d.max_rows, el = d.E / d.ep_size;
+  const int64_t w1n = el * (d.act == MOE_ACT_SWIGLU ? 2 : 1) * d.d_ff * d.d, w2n = el * d.d * d.d_ff;
+  MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {src_token, R, false},
+                            {y_perm, R * d.d, true}, {w1, w1n, true}, {w2, w2n, true},
+                            {offsets, d.E + 1, false}}));
+  MOE_TRY(check_ws(desc, ws, ws_bytes));
+  return do_ffn(d, h, src_token, offsets, w1, w2, y_perm, (char*)ws, (hipStream_t)stream);
 }
 
 MOE_EXPORT moe_status_t moe_unpermute_combine(const moe_layer_desc_t* desc, const void* y_perm,
@@ -239,7 +267,8 @@ MOE_EXPORT moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const vo
     const int64_t w2n = el * d.d * d.d_ff;
     MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {w_router, (int64_t)d.d * d.E, true},
                               {w1, w1n, true}, {w2, w2n, true}, {y, d.T * d.d, true},
-                              {b->x_perm, R * d.d, true}, {b->y_perm, R * d.d, true},
+                              {b->x_perm, b->x_perm ? R * d.d : 0, true},
+                              {b->y_perm, R * d.d, true},
                               {b->logits, TE, false}, {b->topk_idx, Tk, false},
                               {b->topk_gate, Tk, false}, {b->counts, d.E, false},
                               {b->offsets, d.E + 1, false}, {b->dest, Tk, false},
@@ -248,6 +277,7 @@ MOE_EXPORT moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const vo
                               {b->send_displs, d.ep_size, false}, {b->flags, 1, false}}));
   }
   if (router_bias && ((uintptr_t)router_bias & 3u)) return MOE_ERR_ALIGN;
+  if (!b->x_perm) MOE_TRY(check_gather(d));
   MOE_TRY(check_ws(desc, ws, ws_bytes));
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
@@ -255,7 +285,11 @@ MOE_EXPORT moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const vo
                    w, s));
   MOE_TRY(do_permute(d, h, b->topk_idx, b->x_perm, b->counts, b->offsets, b->dest, b->src_token,
                      b->src_slot, b->send_splits, b->send_displs, b->flags, w, s));
-  MOE_TRY(do_ffn(d, b->x_perm, b->offsets, w1, w2, b->y_perm, w, s));
+  // without x_perm the first expert GEMM gathers its rows from h
+  if (b->x_perm)
+    MOE_TRY(do_ffn(d, b->x_perm, nullptr, b->offsets, w1, w2, b->y_perm, w, s));
+  else
+    MOE_TRY(do_ffn(d, h, b->src_token, b->offsets, w1, w2, b->y_perm, w, s));
   return do_combine(d, b->y_perm, b->topk_idx, b->topk_gate, b->dest, y, s);
 }
 

@@ -56,7 +56,8 @@ hipError_t launch_combine(const void* y_perm, const int32_t* idx, const float* g
                           int e_lo, int e_hi, hipStream_t s);
 
 hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
-                              const int32_t* offsets, const void* w1, const void* w2,
-                              void* y_perm, void* act, int4* tiles, hipStream_t s);
+                              const int32_t* rows, const int32_t* offsets, const void* w1,
+                              const void* w2, void* y_perm, void* act, int4* tiles,
+                              hipStream_t s);
 
 }  // namespace moe

@@ -70,12 +70,15 @@ __device__ __forceinline__ int main_tile_end(int total, int G) {
   return (tail > 0 && 2 * tail <= G) ? full : total;
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF>
+// GA (gathered A): A row i of the grouped operand is row rows[i] of A, so the
+// token rows need not be copied into expert order first (the fused layer
+// call's dispatch); otherwise A is the expert-ordered matrix itself.
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ W, bf16* __restrict__ C,
-    const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr, int N, int K,
-    int64_t w_stride, int n_n, int64_t ldc) {
-  using TG = TileGemmDL<BM, BN, WM, WN, EPI, BK, MF>;
+    const bf16* __restrict__ A, const int32_t* __restrict__ rows, const bf16* __restrict__ W,
+    bf16* __restrict__ C, const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr,
+    int N, int K, int64_t w_stride, int n_n, int64_t ldc) {
+  using TG = TileGemmDL<BM, BN, WM, WN, EPI, BK, MF, GA>;
   __shared__ __attribute__((aligned(1024))) bf16 lds[TG::LDS_ELEMS];
   const int n_m = *n_mt_ptr;
   const int G = gridDim.x;
@@ -89,7 +92,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
     tile_coords<GROUP_M>(v, n_m, n_n, mt, nt);
     const int4 e = tile_entry(tiles, mt);   // expert, first row, end row
     const int ex = e.x, ey = e.y, ez = e.z;
-    t.a = A + (int64_t)ey * K;
+    t.a = GA ? A : A + (int64_t)ey * K;
+    t.rows = GA ? rows + ey : nullptr;
     t.a_rows = ez - ey;
     t.n0 = nt * BN;
     t.b = W + (int64_t)ex * w_stride + (int64_t)t.n0 * K;
@@ -103,12 +107,12 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
 // The leftover tiles of the kernel above (same tile table, same order), as
 // half-height tiles of HM = BM / 2 rows: unit u is half u & 1 of tile
 // main_tile_end + u / 2. G is the main kernel's grid size.
-template <int HM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF>
+template <int HM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ W, bf16* __restrict__ C,
-    const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr, int N, int K,
-    int64_t w_stride, int n_n, int64_t ldc, int G) {
-  using TG = TileGemmDL<HM, BN, WM, WN, EPI, BK, MF>;
+    const bf16* __restrict__ A, const int32_t* __restrict__ rows, const bf16* __restrict__ W,
+    bf16* __restrict__ C, const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr,
+    int N, int K, int64_t w_stride, int n_n, int64_t ldc, int G) {
+  using TG = TileGemmDL<HM, BN, WM, WN, EPI, BK, MF, GA>;
   __shared__ __attribute__((aligned(1024))) bf16 lds[TG::LDS_ELEMS];
   const int n_m = *n_mt_ptr;
   const int total = n_m * n_n;
@@ -125,7 +129,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
       const int4 e = tile_entry(tiles, mt);
       const int ex = e.x, ey = e.y + (u & 1) * HM, ez = e.z;
       if (ey >= ez) continue;
-      t.a = A + (int64_t)ey * K;
+      t.a = GA ? A : A + (int64_t)ey * K;
+      t.rows = GA ? rows + ey : nullptr;
       t.a_rows = min(ez - ey, HM);
       t.n0 = nt * BN;
       t.b = W + (int64_t)ex * w_stride + (int64_t)t.n0 * K;
@@ -138,22 +143,23 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
   TG::run_tiles(get, N, K, C, ldc, lds);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF>
-static hipError_t grouped_gemm_dl_launch(const bf16* A, const bf16* W, bf16* C,
-                                         const int4* tiles, const int* n_mt, int N, int K,
-                                         int64_t w_stride, int64_t ldc, int64_t max_mtiles,
-                                         int per_cu, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA = false>
+static hipError_t grouped_gemm_dl_launch(const bf16* A, const int32_t* rows, const bf16* W,
+                                         bf16* C, const int4* tiles, const int* n_mt, int N,
+                                         int K, int64_t w_stride, int64_t ldc,
+                                         int64_t max_mtiles, int per_cu, hipStream_t s) {
   const int n_n = (N + BN - 1) / BN;
   const int64_t ub = max_mtiles * n_n;
   int64_t G = min(((ub + 7) / 8) * 8, (int64_t)device_cu_count() * per_cu);
   G = max((int64_t)8, G / 8 * 8);
-  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BN, WM, WN, EPI, BK, GROUP_M, MF>), dim3((unsigned)G),
-                     dim3(64 * WM * WN), 0, s, A, W, C, tiles, n_mt, N, K, w_stride, n_n, ldc);
+  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>),
+                     dim3((unsigned)G), dim3(64 * WM * WN), 0, s, A, rows, W, C, tiles, n_mt, N,
+                     K, w_stride, n_n, ldc);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((grouped_gemm_tail_kernel<BM / 2, BN, WM, WN, EPI, BK, GROUP_M, MF>),
-                     dim3((unsigned)G), dim3(64 * WM * WN), 0, s, A, W, C, tiles, n_mt, N, K,
-                     w_stride, n_n, ldc, (int)G);
+  hipLaunchKernelGGL((grouped_gemm_tail_kernel<BM / 2, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>),
+                     dim3((unsigned)G), dim3(64 * WM * WN), 0, s, A, rows, W, C, tiles, n_mt, N,
+                     K, w_stride, n_n, ldc, (int)G);
   return hipGetLastError();
 }
 
@@ -165,9 +171,9 @@ constexpr int kF32BM = 64;
 
 template <int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
-    const float* __restrict__ A, const float* __restrict__ W, float* __restrict__ C,
-    const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr, int N, int K,
-    int64_t w_stride, int64_t ldc) {
+    const float* __restrict__ A, const int32_t* __restrict__ a_rows, const float* __restrict__ W,
+    float* __restrict__ C, const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr,
+    int N, int K, int64_t w_stride, int64_t ldc) {
   const int mt = blockIdx.x;
   if (mt >= *n_mt_ptr) return;
   const int4 t = tiles[mt];
@@ -181,7 +187,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     for (int q = threadIdx.x; q < 64 * 16; q += 256) {
       int r = q >> 4, kk = q & 15;
       int k = k0 + kk;
-      As[kk][r] = (r < rows && k < K) ? A[(int64_t)(t.y + r) * K + k] : 0.f;
+      const int64_t ar = r < rows ? (a_rows ? a_rows[t.y + r] : t.y + r) : 0;
+      As[kk][r] = (r < rows && k < K) ? A[ar * K + k] : 0.f;
       int n = n0 + r;
       Bs[kk][r] = (n < N && k < K) ? Wb[(int64_t)n * K + k] : 0.f;
       if (EPI == 2) Us[kk][r] = (n < N && k < K) ? Wb[(int64_t)(N + n) * K + k] : 0.f;
@@ -216,13 +223,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
 }
 
 template <int EPI>
-static hipError_t grouped_gemm_f32_launch(const float* A, const float* W, float* C,
-                                          const int4* tiles, const int* n_mt, int N, int K,
-                                          int64_t w_stride, int64_t ldc, int64_t max_mtiles,
-                                          hipStream_t s) {
+static hipError_t grouped_gemm_f32_launch(const float* A, const int32_t* a_rows, const float* W,
+                                          float* C, const int4* tiles, const int* n_mt, int N,
+                                          int K, int64_t w_stride, int64_t ldc,
+                                          int64_t max_mtiles, hipStream_t s) {
   dim3 grid((unsigned)max_mtiles, (unsigned)((N + 63) / 64));
-  hipLaunchKernelGGL(grouped_gemm_f32_kernel<EPI>, grid, dim3(256), 0, s, A, W, C, tiles, n_mt,
-                     N, K, w_stride, ldc);
+  hipLaunchKernelGGL(grouped_gemm_f32_kernel<EPI>, grid, dim3(256), 0, s, A, a_rows, W, C, tiles,
+                     n_mt, N, K, w_stride, ldc);
   return hipGetLastError();
 }
 
@@ -241,9 +248,12 @@ int64_t gemm_max_mtiles(const moe_layer_desc_t& d) {
   return (rows + kF32BM - 1) / kF32BM + el;  // the smallest BM of any path
 }
 
+// x_perm: the expert-ordered rows, or (gathered, rows != null) the token rows
+// h, read through rows = src_token.
 hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
-                              const int32_t* offsets, const void* w1, const void* w2,
-                              void* y_perm, void* act, int4* tiles, hipStream_t s) {
+                              const int32_t* rows, const int32_t* offsets, const void* w1,
+                              const void* w2, void* y_perm, void* act, int4* tiles,
+                              hipStream_t s) {
   const int el = desc.E / desc.ep_size;
   const int e_lo = desc.ep_rank * el;
   const int64_t max_mt = gemm_max_mtiles(desc);
@@ -257,30 +267,39 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
                        desc.max_rows, kGemmBM, tiles, n_mt);
     const int64_t mt_ub = (desc.max_rows + kGemmBM - 1) / kGemmBM + el;
     const bf16* X = (const bf16*)x_perm;
+    const bf16* W1 = (const bf16*)w1;
     bf16* H = (bf16*)act;
-    if (swiglu)
+    const int64_t s1 = (int64_t)w1_rows * d;
+    if (swiglu && rows)
+      err = grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_SWIGLU_BF16, 64, kGemmGroupM, 16, true>(
+          X, rows, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s);
+    else if (swiglu)
       err = grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_SWIGLU_BF16, 64, kGemmGroupM, 16>(
-          X, (const bf16*)w1, H, tiles, n_mt, dff, d, (int64_t)w1_rows * d, dff, mt_ub, 1, s);
+          X, nullptr, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s);
+    else if (rows)
+      err = grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_RELU_BF16, 64, kGemmGroupM, 16, true>(
+          X, rows, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s);
     else
       err = grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_RELU_BF16, 64, kGemmGroupM, 16>(
-          X, (const bf16*)w1, H, tiles, n_mt, dff, d, (int64_t)w1_rows * d, dff, mt_ub, 1, s);
+          X, nullptr, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s);
     if (err != hipSuccess) return err;
     return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_STORE_BF16, 64, kGemmGroupM, 16>(
-        H, (const bf16*)w2, (bf16*)y_perm, tiles, n_mt, d, dff, (int64_t)d * dff, d, mt_ub, 1, s);
+        H, nullptr, (const bf16*)w2, (bf16*)y_perm, tiles, n_mt, d, dff, (int64_t)d * dff, d,
+        mt_ub, 1, s);
   }
   hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,
                      desc.max_rows, kF32BM, tiles, n_mt);
   const float* X = (const float*)x_perm;
   float* H = (float*)act;
   if (swiglu)
-    err = grouped_gemm_f32_launch<2>(X, (const float*)w1, H, tiles, n_mt, dff, d,
+    err = grouped_gemm_f32_launch<2>(X, rows, (const float*)w1, H, tiles, n_mt, dff, d,
                                      (int64_t)w1_rows * d, dff, max_mt, s);
   else
-    err = grouped_gemm_f32_launch<1>(X, (const float*)w1, H, tiles, n_mt, dff, d,
+    err = grouped_gemm_f32_launch<1>(X, rows, (const float*)w1, H, tiles, n_mt, dff, d,
                                      (int64_t)w1_rows * d, dff, max_mt, s);
   if (err != hipSuccess) return err;
-  return grouped_gemm_f32_launch<0>(H, (const float*)w2, (float*)y_perm, tiles, n_mt, d, dff,
-                                    (int64_t)d * dff, d, max_mt, s);
+  return grouped_gemm_f32_launch<0>(H, nullptr, (const float*)w2, (float*)y_perm, tiles, n_mt, d,
+                                    dff, (int64_t)d * dff, d, max_mt, s);
 }
 
 }  // namespace moe

@@ -71,6 +71,8 @@ struct GemmTile {
   int n0;           // first output column
   int64_t c_row;    // output row of the tile's first A row
   int nk;           // K slices (of BK) to multiply
+  const int32_t* rows;   // gathered A rows only: the tile's A row i is row rows[i]
+                         // of the matrix at `a` (then `a` is that matrix's base)
 };
 
 // Persistent tile loop of one workgroup: run_tiles(get, ...) multiplies the
@@ -78,7 +80,7 @@ struct GemmTile {
 // two LDS buffers as one sequence that runs across tile boundaries: the next
 // tile's first slices are already in flight while the current tile's
 // epilogue converts and stores its accumulators.
-template <int BM, int BN, int WM, int WN, int EPI, int BK = 64, int MF = 16>
+template <int BM, int BN, int WM, int WN, int EPI, int BK = 64, int MF = 16, bool GA = false>
 struct TileGemmDL {
   using L = SliceLayout<BK>;
   static constexpr int NT = 64 * WM * WN;
@@ -103,6 +105,8 @@ struct TileGemmDL {
   static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be a multiple of the MFMA tile");
   static_assert(BK % 32 == 0 && NSUB >= 2, "two or more MFMA sub-steps per K slice");
   static_assert(BM % L::RPL == 0, "a load must not straddle the A and B rows");
+  // gathered A rows keep one swizzle key per load parity (16 rows per key cycle)
+  static_assert(!GA || 2 * L::RPL == L::RPB * L::CPR, "gathered rows need BK = 64");
 
   // C is bf16 (row stride ldc) for the expert epilogues; for EPI_ROUTER_F32 it
   // is float, bias (or null) is added and only columns < n_store are written.
@@ -125,9 +129,17 @@ struct TileGemmDL {
     // (wave * LPW + i) * RPL .. + RPL - 1 of a slice; whether those are A or
     // weight rows is uniform across the wave (RPL divides BM).
     bool is_a[LPW];
-    uint32_t off[LPW];   // per-lane byte offset from the tile's a / b pointer
+    // per-lane byte offset from the tile's a / b pointer; for gathered A rows
+    // the row index itself, made a byte offset when the slice is fetched (so
+    // the row-index load has a whole slice of MFMAs to arrive)
+    uint32_t off[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) is_a[i] = (wave * LPW + i) * L::RPL < BM;
+    // gathered A rows: byte offset of this lane's 16-byte chunk, for loads of
+    // even and odd index in the slice
+    const uint32_t chunk_even = GA ? (uint32_t)(L::swz(lane / L::CPR, lane % L::CPR) * 16) : 0u;
+    const uint32_t chunk_odd =
+        GA ? (uint32_t)(L::swz(L::RPL + lane / L::CPR, lane % L::CPR) * 16) : 0u;
     auto set_offsets = [&](const GemmTile& t) {
       // the lane id is re-read here (volatile, so it stays inside the tile
       // loop); otherwise the compiler keeps every load's row and chunk live
@@ -141,6 +153,10 @@ struct TileGemmDL {
         int row;
         if (is_a[i]) {
           row = r < t.a_rows ? r : t.a_rows - 1;
+          if constexpr (GA) {
+            off[i] = (uint32_t)t.rows[row];
+            continue;
+          }
         } else {
           const int q = r - BM;
           const int ql = (GATED && q >= BN) ? q - BN : q;
@@ -157,7 +173,10 @@ struct TileGemmDL {
       const uint32_t ko = (uint32_t)kt * (BK * 2);
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
-        const char* src = reinterpret_cast<const char*>(is_a[i] ? t.a : t.b) + (off[i] + ko);
+        uint32_t o = off[i];
+        if (GA && is_a[i])
+          o = o * (uint32_t)(K * 2) + (((wave * LPW + i) & 1) ? chunk_odd : chunk_even);
+        const char* src = reinterpret_cast<const char*>(is_a[i] ? t.a : t.b) + (o + ko);
         __builtin_amdgcn_global_load_lds(src, base + i * L::RPL * BK, 16, 0, 0);
       }
     };

@@ -128,7 +128,9 @@ moe_status_t moe_topk_from_logits(const moe_layer_desc_t* desc, const float* log
                                   void* stream);
 
 /* Permute: group the (token, slot) assignments of topk_idx [T,k] by expert
- * and copy the token rows into x_perm [max_rows,d].
+ * and copy the token rows into x_perm [max_rows,d]. x_perm may be NULL: then
+ * only the plan below is made and no row is copied (the rows can be read in
+ * place by moe_grouped_ffn_gather).
  * Dispatch page ("Follow one documented dispatch and return path"): counts
  * and communication splits from the routing map, tokens rearranged per
  * expert. Capacity page and the repeatability page's capacity passage: at
@@ -162,6 +164,19 @@ moe_status_t moe_grouped_ffn(const moe_layer_desc_t* desc, const void* x_perm,
                              const int32_t* offsets, const void* w1, const void* w2,
                              void* y_perm, void* ws, size_t ws_bytes, void* stream);
 
+/* The same grouped expert FFN with dispatch fused into the first GEMM: row r
+ * of an expert's group is read straight from h [T,d] at token src_token[r]
+ * (the inverse map moe_permute writes), so the rows are never copied into
+ * x_perm. "Dropless MoE Is a Runtime Problem as Much as a Model Design",
+ * expert-parallelism paragraph: fusing dispatch into the expert computation
+ * removes an intermediate write and its read. Results are bit-identical to
+ * moe_grouped_ffn on x_perm. bf16 needs T*d*2 bytes below 4 GiB
+ * (MOE_ERR_SHAPE otherwise). */
+moe_status_t moe_grouped_ffn_gather(const moe_layer_desc_t* desc, const void* h,
+                                    const int32_t* src_token, const int32_t* offsets,
+                                    const void* w1, const void* w2, void* y_perm, void* ws,
+                                    size_t ws_bytes, void* stream);
+
 /* Unpermute + combine: y[t] = sum_j topk_gate[t,j] * y_perm[dest[t,j]] over
  * slots with dest >= 0 whose expert is local, summed in float32 in slot
  * order, rounded once to dtype. Tokens with no such slot get zeros (the
@@ -172,7 +187,10 @@ moe_status_t moe_unpermute_combine(const moe_layer_desc_t* desc, const void* y_p
                                    const int32_t* dest, void* y, void* stream);
 
 /* Buffers of the fused call; all are required device pointers with the
- * shapes given above. */
+ * shapes given above, except x_perm, which may be NULL: then the fused call
+ * makes only the plan in its permute step and the first expert GEMM reads
+ * the rows from h (as moe_grouped_ffn_gather); x_perm is then not produced,
+ * which also means no expert-parallel send buffer. */
 typedef struct moe_layer_buffers {
   float* logits;        /* [T,E] */
   int32_t* topk_idx;    /* [T,k] */
@@ -191,7 +209,8 @@ typedef struct moe_layer_buffers {
 
 /* The whole layer in one call: route, permute, grouped FFN, unpermute +
  * combine, enqueued back to back on `stream` with no host synchronisation.
- * Equivalent to the four stage calls in order. */
+ * Equivalent to the four stage calls in order (with buffers->x_perm NULL:
+ * moe_permute without x_perm, then moe_grouped_ffn_gather). */
 moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const void* h, const void* w_router,
                                const float* router_bias, const void* w1, const void* w2, void* y,
                                const moe_layer_buffers_t* buffers, void* ws, size_t ws_bytes,

@@ -23,7 +23,8 @@ def _declared():
 
 @pytest.fixture(scope="module")
 def G():
-    from grouped_expert_ffn_amd import build as B
+    import __graft_entry__ as entry
+    B = entry._build_module()   # by path: the package import needs a built library
     if not os.path.exists(B.LIB):
         B.build()
     import grouped_expert_ffn_amd as G
@@ -98,6 +99,19 @@ def test_bf16_weights_beyond_32bit_tile_offsets_rejected(G):
     assert G.workspace_size(ok) > 0
     too_wide = G.make_desc(64, 8192, 8, 2, 131072, "bf16", "softmax", "swiglu")
     assert _call_route(G, too_wide) == 2
+
+
+def test_gather_rejects_token_rows_beyond_32bit_offsets(G):
+    """The gathered first GEMM addresses bf16 token rows of h with 32-bit
+    byte offsets: T*d*2 must stay below 4 GiB; nothing is launched."""
+    lib = G._lib
+    p = ctypes.c_void_p
+    big = G.make_desc(1 << 19, 4096, 8, 2, 128, "bf16", "softmax", "swiglu")
+    st = lib.moe_grouped_ffn_gather(ctypes.byref(big), p(1024), p(2048), p(4096), p(8192),
+                                    p(16384), p(32768), p(65536), 1 << 40, None)
+    assert st == 2
+    assert lib.moe_grouped_ffn_gather(None, p(1024), p(2048), p(4096), p(8192), p(16384),
+                                      p(32768), p(65536), 1 << 40, None) == 1
 
 
 def test_fp32_allows_any_width(G):
