@@ -13,7 +13,7 @@ two MFMA GEMMs), per-stage figures, and the CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--skip-cpu-baseline]
-                    [--cold-steps N]
+                    [--cold-steps N] [--gather] [--ablation]
 
 After the timed steps, N more steps run one by one, each after a 512 MiB
 write that evicts the 256 MiB last-level cache (MALL); their event-timed
@@ -105,6 +105,92 @@ def cpu_baseline(cfg, inp, capacity, sample_tokens, min_seconds):
                       f"float64 numpy oracle, {runs} run(s) in {total:.1f} s"}
 
 
+def ablation_baselines(G, desc, x_perm, offsets, w1, w2, reps=5):
+    """The grouped expert FFN beside two ways of running the same experts
+    that it replaces ("Dropless MoE Is a Runtime Problem as Much as a Model
+    Design", grouped GEMM paragraph: no launch per expert, no padding to a
+    common capacity), all with this library's kernels on the same plan:
+
+      per_expert: one grouped-FFN call per local expert on its own rows;
+      padded:     every local expert padded to C = the largest group, as one
+                  grouped call over uniform groups ([E_loc, C, d] layout).
+
+    Each real row goes through the same tile decomposition and K order, so
+    all three give the same bits. Returns the timings (median of `reps`,
+    HIP events on the current stream) and the three y_perm copies."""
+    import torch
+    dt = x_perm.dtype
+    el = desc.E // desc.ep_size
+    lo = desc.ep_rank * el
+    offs = offsets.cpu().numpy().astype(np.int64)
+    rows0 = min(int(offs[lo]), desc.max_rows)
+    n = [max(0, min(int(offs[lo + e + 1]), desc.max_rows) - min(int(offs[lo + e]), desc.max_rows))
+         for e in range(el)]
+    first = [min(int(offs[lo + e]), desc.max_rows) for e in range(el)]
+    d = desc.d
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    # grouped: the library's call
+    ws = G.alloc_workspace(desc)
+    y_grp = torch.zeros((desc.max_rows, d), dtype=dt, device="cuda")
+    t_grp = timed(lambda: G.grouped_ffn(desc, x_perm, offsets, w1, w2, y_grp, ws))
+
+    # per expert: E_loc calls, each a one-expert layer over that expert's rows
+    y_pe = torch.zeros_like(y_grp)
+    calls = []
+    n_max = max(n + [1])
+    d1 = G.make_desc(n_max, d, 1, 1, desc.d_ff, "bf16" if desc.dtype == 1 else "f32",
+                     "softmax", "swiglu" if desc.act == 1 else "relu", max_rows=n_max)
+    ws1 = G.alloc_workspace(d1)
+    for e in range(el):
+        if n[e] == 0:
+            continue
+        de = G.make_desc(n[e], d, 1, 1, desc.d_ff, "bf16" if desc.dtype == 1 else "f32",
+                         "softmax", "swiglu" if desc.act == 1 else "relu", max_rows=n[e])
+        oe = torch.tensor([0, n[e]], dtype=torch.int32, device="cuda")
+        calls.append((de, x_perm[first[e]:first[e] + n[e]], oe, w1[e:e + 1], w2[e:e + 1],
+                      y_pe[first[e]:first[e] + n[e]]))
+
+    def per_expert():
+        for de, xe, oe, a, b, ye in calls:
+            G.grouped_ffn(de, xe, oe, a, b, ye, ws1)
+    t_pe = timed(per_expert)
+
+    # padded: [E_loc, C, d] with C the largest group, zero rows past each group
+    C = max(n + [1])
+    x_pad = torch.zeros((el * C, d), dtype=dt, device="cuda")
+    for e in range(el):
+        x_pad[e * C:e * C + n[e]] = x_perm[first[e]:first[e] + n[e]]
+    dp = G.make_desc(el * C, d, el, 1, desc.d_ff, "bf16" if desc.dtype == 1 else "f32",
+                     "softmax", "swiglu" if desc.act == 1 else "relu", max_rows=el * C)
+    op = torch.arange(0, (el + 1) * C, C, dtype=torch.int32, device="cuda")
+    y_pad = torch.empty((el * C, d), dtype=dt, device="cuda")
+    wsp = G.alloc_workspace(dp)
+    t_pad = timed(lambda: G.grouped_ffn(dp, x_pad, op, w1, w2, y_pad, wsp))
+    y_pad_rows = torch.zeros_like(y_grp)
+    for e in range(el):
+        y_pad_rows[first[e]:first[e] + n[e]] = y_pad[e * C:e * C + n[e]]
+    real = sum(n)
+    info = {"grouped_ms": t_grp, "per_expert_ms": t_pe, "per_expert_calls": len(calls),
+            "padded_ms": t_pad, "padded_rows": el * C, "real_rows": real,
+            "padding_frac": 1.0 - real / max(1, el * C), "largest_group": C,
+            "first_local_row": rows0}
+    return info, y_grp, y_pe, y_pad_rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +204,9 @@ def main():
     ap.add_argument("--gather", action="store_true",
                     help="fused dispatch: permute makes only the plan and the first expert GEMM "
                          "reads token rows from h through src_token")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also time the grouped FFN beside a launch per expert and the padded "
+                         "capacity layout, with the same kernels on the same plan")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps, each after a 512 MiB write that evicts the 256 MiB MALL, "
                          "timed one by one with events (reported beside the main figure)")
@@ -262,6 +351,18 @@ def main():
         "env": {"device": torch.cuda.get_device_name(), "torch": torch.__version__,
                 "hip": torch.version.hip, "library_sha": library_sha()},
     }
+    if args.ablation:
+        b_x = b.x_perm
+        if gather:   # the baselines run on expert-ordered rows
+            b_x = torch.empty((desc.max_rows, cfg.d), dtype=dt, device="cuda")
+            G.permute(desc, h, b.topk_idx, b_x, b.counts, b.offsets, b.dest, b.src_token,
+                      b.src_slot, b.send_splits, b.send_displs, b.flags, ws)
+        info, y_grp, y_pe, y_pad = ablation_baselines(G, desc, b_x, b.offsets, w1, w2)
+        flops_useful = ffn_flops(n_local, cfg.d, cfg.d_ff, cfg.act)
+        for key in ("grouped", "per_expert", "padded"):
+            info[key + "_useful_TFLOPs"] = flops_useful / (info[key + "_ms"] / 1e3) / 1e12
+        info["bitwise_equal"] = bool(torch.equal(y_grp, y_pe) and torch.equal(y_grp, y_pad))
+        out["ablation"] = info
     if not args.skip_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, capacity, args.cpu_sample_tokens,
                                           args.cpu_min_seconds)

@@ -104,3 +104,26 @@ def test_fused_call_without_x_perm_full_mixtral_layer():
     desc, dv = upload_layer(G, cfg, inp)
     (y_a, _), (y_g, _) = _both(G, desc, dv)
     assert torch.equal(y_a, y_g)
+
+
+@pytest.mark.parametrize("name,T", [("small_bf16", 1024), ("finegrained_bf16", 1024),
+                                    ("ep_share_bf16", 512), ("tiny_fp32", 64)])
+def test_ablation_baselines_give_the_grouped_bits(name, T):
+    """The benchmark's baselines (one grouped call per expert; the padded
+    [E_loc, C, d] layout) run the same kernels on the same rows, so they
+    must reproduce the grouped call's output bits."""
+    import bench
+    G = lib()
+    cfg = small_layer_config(CONFIGS[name], T)
+    inp = make_inputs(cfg)
+    desc, dv = upload_layer(G, cfg, inp)
+    y, b, _ = run_layer(G, desc, dv)
+    info, y_grp, y_pe, y_pad = bench.ablation_baselines(G, desc, b.x_perm, b.offsets,
+                                                        dv["w1"], dv["w2"], reps=1)
+    say(f"ablation {name}: {info}")
+    el = cfg.E // cfg.ep_size
+    lo, hi = host(b.offsets)[[cfg.ep_rank * el, (cfg.ep_rank + 1) * el]]
+    assert torch.equal(y_grp[lo:hi], b.y_perm[lo:hi])
+    assert torch.equal(y_pe[lo:hi], y_grp[lo:hi])
+    assert torch.equal(y_pad[lo:hi], y_grp[lo:hi])
+    assert info["real_rows"] == int(hi - lo)
