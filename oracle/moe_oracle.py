@@ -228,6 +228,45 @@ def permute(h, dest, rows=None):
     return x
 
 
+def dedup_pack(idx, dest, E, ep_size):
+    """Expert-parallel send packing with token deduplication.
+
+    "Dropless MoE Is a Runtime Problem as Much as a Model Design",
+    expert-parallelism paragraph: when top-k routing sends one token to
+    several experts on the same destination, the token needs to cross the
+    network only once. Here every (destination rank, token) pair with at
+    least one sent slot gets one send row; a slot is sent when the plan
+    materialised it (dest >= 0), and its rank is its expert's owner,
+    expert // (E / ep_size). Pair rows are ordered by rank, then token, so
+    each rank's rows form one contiguous segment.
+
+    Returns a dict:
+      pair_dest[T,k]   send row of each slot's (rank, token) pair; -1 unsent
+      pair_token[P]    token of each pair row
+      pair_splits[ep], pair_displs[ep]   rows and first row of each rank
+    """
+    idx = np.asarray(idx, np.int64)
+    dest = np.asarray(dest, np.int64)
+    T, k = idx.shape
+    if E % ep_size:
+        raise ValueError("E must be a multiple of ep_size")
+    el = E // ep_size
+    sent = dest >= 0
+    pairs = sorted({(int(idx[t, j]) // el, t) for t in range(T) for j in range(k) if sent[t, j]})
+    row = {p: i for i, p in enumerate(pairs)}
+    pair_dest = np.full((T, k), -1, np.int64)
+    for t in range(T):
+        for j in range(k):
+            if sent[t, j]:
+                pair_dest[t, j] = row[(int(idx[t, j]) // el, t)]
+    pair_token = np.array([t for _, t in pairs], np.int64)
+    ranks = np.array([r for r, _ in pairs], np.int64)
+    pair_splits = np.array([int(np.count_nonzero(ranks == r)) for r in range(ep_size)], np.int64)
+    pair_displs = np.concatenate([[0], np.cumsum(pair_splits)[:-1]]).astype(np.int64)
+    return dict(pair_dest=pair_dest, pair_token=pair_token, pair_splits=pair_splits,
+                pair_displs=pair_displs)
+
+
 # ---------------------------------------------------------------------------
 # Experts
 # ---------------------------------------------------------------------------
