@@ -13,7 +13,7 @@ two MFMA GEMMs), per-stage figures, and the CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--skip-cpu-baseline]
-                    [--cold-steps N] [--gather] [--ablation]
+                    [--cold-steps N] [--gather] [--ablation] [--dedup]
 
 After the timed steps, N more steps run one by one, each after a 512 MiB
 write that evicts the 256 MiB last-level cache (MALL); their event-timed
@@ -191,6 +191,73 @@ def ablation_baselines(G, desc, x_perm, offsets, w1, w2, reps=5):
     return info, y_grp, y_pe, y_pad_rows
 
 
+def dedup_bench(G, desc, h, b, w1, w2, ws, reps=10):
+    """Expert-parallel packing with one send row per (destination rank,
+    token) pair, timed on the step's own plan beside the plan-only permute,
+    and the local experts run from the deduplicated rows; their output rows
+    are compared bit for bit with the step's y_perm."""
+    import torch
+    P, dt = G.max_pairs(desc), G.torch_dtype(desc)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    send = torch.empty((P, desc.d), dtype=dt, device="cuda")
+    pair_dest = torch.empty((desc.T, desc.k), **i32)
+    pair_token = torch.empty((P,), **i32)
+    splits = torch.empty((desc.ep_size,), dtype=torch.int64, device="cuda")
+    displs = torch.empty_like(splits)
+    recv = torch.empty((desc.max_rows,), **i32)
+    y2 = torch.empty_like(b.y_perm)
+    stream = torch.cuda.current_stream()
+    c = [torch.empty_like(b.counts), torch.empty_like(b.offsets), torch.empty_like(b.dest),
+         torch.empty_like(b.src_token), torch.empty_like(b.src_slot),
+         torch.empty_like(b.send_splits), torch.empty_like(b.send_displs),
+         torch.zeros_like(b.flags)]
+
+    def plan_only():
+        G.permute(desc, h, b.topk_idx, None, *c, ws)
+
+    def pack():
+        G.pack_dedup(desc, h, b.topk_idx, b.dest, b.src_token, b.src_slot, b.offsets, send,
+                     pair_dest, pair_token, splits, displs, recv, ws)
+
+    def ffn():
+        G.grouped_ffn_gather(desc, send, recv, b.offsets, w1, w2, y2, ws)
+
+    def timed(fn):
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+    info = {"plan_only_permute_ms": timed(plan_only), "pack_dedup_ms": timed(pack)}
+    info["grouped_ffn_from_pairs_ms"] = timed(ffn)
+    offs = b.offsets.cpu().numpy().astype(np.int64)
+    el = desc.E // desc.ep_size
+    lo = min(int(offs[desc.ep_rank * el]), desc.max_rows)
+    hi = min(int(offs[(desc.ep_rank + 1) * el]), desc.max_rows)
+    n_pairs = int(splits.sum().item())
+    n_slots = int((b.dest >= 0).sum().item())
+    n_tok = int(torch.unique(pair_token[:n_pairs]).numel())
+    eb = 2 if desc.dtype == G.DTYPE_BF16 else 4
+    row = desc.d * eb
+    Tk = desc.T * desc.k
+    # reads each sent token's row once and writes each pair row; ids: idx and
+    # dest read by three kernels, pid / first_row / pair_dest written (4 B each)
+    pack_bytes = (n_tok + n_pairs) * row + 36 * Tk + 12 * n_pairs
+    info.update({
+        "send_rows_one_per_slot": n_slots, "send_rows_one_per_pair": n_pairs,
+        "payload_bytes_one_per_slot": n_slots * row, "payload_bytes_one_per_pair": n_pairs * row,
+        "payload_reduction": 1.0 - n_pairs / max(n_slots, 1),
+        "pair_splits": splits.cpu().tolist(),
+        "pack_GBs": pack_bytes / (info["pack_dedup_ms"] / 1e3) / 1e9,
+        "ffn_rows_bitwise_equal": bool(torch.equal(y2[lo:hi], b.y_perm[lo:hi]))})
+    return info
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,6 +274,9 @@ def main():
     ap.add_argument("--ablation", action="store_true",
                     help="also time the grouped FFN beside a launch per expert and the padded "
                          "capacity layout, with the same kernels on the same plan")
+    ap.add_argument("--dedup", action="store_true",
+                    help="also time expert-parallel packing with one send row per "
+                         "(rank, token) pair and the local experts run from those rows")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps, each after a 512 MiB write that evicts the 256 MiB MALL, "
                          "timed one by one with events (reported beside the main figure)")
@@ -363,6 +433,8 @@ def main():
             info[key + "_useful_TFLOPs"] = flops_useful / (info[key + "_ms"] / 1e3) / 1e12
         info["bitwise_equal"] = bool(torch.equal(y_grp, y_pe) and torch.equal(y_grp, y_pad))
         out["ablation"] = info
+    if args.dedup:
+        out["dedup"] = dedup_bench(G, desc, h, b, w1, w2, ws)
     if not args.skip_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, capacity, args.cpu_sample_tokens,
                                           args.cpu_min_seconds)

@@ -30,8 +30,8 @@ FLAG_ROW_OVERFLOW, FLAG_BAD_EXPERT_ID, FLAG_NONFINITE_LOGIT, FLAG_DROPPED = 1, 2
 
 EXPORTED = ("moe_capacity_from_factor", "moe_workspace_size", "moe_route",
             "moe_topk_from_logits", "moe_permute", "moe_grouped_ffn",
-            "moe_grouped_ffn_gather", "moe_unpermute_combine", "moe_layer_forward",
-            "moe_status_str")
+            "moe_grouped_ffn_gather", "moe_pack_dedup", "moe_unpermute_combine",
+            "moe_layer_forward", "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -70,6 +70,7 @@ def _load():
         "moe_permute": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_grouped_ffn": (I32, [D, P, P, P, P, P, P, SZ, P]),
         "moe_grouped_ffn_gather": (I32, [D, P, P, P, P, P, P, P, SZ, P]),
+        "moe_pack_dedup": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_unpermute_combine": (I32, [D, P, P, P, P, P, P]),
         "moe_layer_forward": (I32, [D, P, P, P, P, P, P, ctypes.POINTER(LayerBuffers), P, SZ, P]),
         "moe_status_str": (ctypes.c_char_p, [I32]),
@@ -258,16 +259,45 @@ def grouped_ffn(desc, x_perm, offsets, w1, w2, y_perm, ws, stream=None):
 
 
 def grouped_ffn_gather(desc, h, src_token, offsets, w1, w2, y_perm, ws, stream=None):
+    """h: the token rows [T, d], or a deduplicated send buffer [max_pairs, d]
+    (then src_token is the recv_rows of moe_pack_dedup)."""
     dt = torch_dtype(desc)
     s1, s2 = _w_shapes(desc)
     T, R, d = desc.T, desc.max_rows, desc.d
+    if h is not None and h.shape[0] not in (T, max_pairs(desc)):
+        raise ValueError(f"h must have {T} or {max_pairs(desc)} rows")
     wsp, wsn = _ws(ws)
     _check(_lib.moe_grouped_ffn_gather(
-        ctypes.byref(desc), _ptr(h, "h", dt, (T, d)),
+        ctypes.byref(desc), _ptr(h, "h", dt, (h.shape[0] if h is not None else T, d)),
         _ptr(src_token, "src_token", torch.int32, (R,)),
         _ptr(offsets, "offsets", torch.int32, (desc.E + 1,)),
         _ptr(w1, "w1", dt, s1), _ptr(w2, "w2", dt, s2), _ptr(y_perm, "y_perm", dt, (R, d)),
         wsp, wsn, _stream(stream)), "moe_grouped_ffn_gather")
+
+
+def max_pairs(desc) -> int:
+    """Rows of a deduplicated send buffer: T * min(k, ep_size)."""
+    return desc.T * min(desc.k, desc.ep_size)
+
+
+def pack_dedup(desc, h, topk_idx, dest, src_token, src_slot, offsets, send_buf, pair_dest,
+               pair_token, pair_splits, pair_displs, recv_rows, ws, stream=None):
+    dt = torch_dtype(desc)
+    T, d, k, R, P = desc.T, desc.d, desc.k, desc.max_rows, max_pairs(desc)
+    wsp, wsn = _ws(ws)
+    _check(_lib.moe_pack_dedup(
+        ctypes.byref(desc), _ptr(h, "h", dt, (T, d)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)), _ptr(dest, "dest", torch.int32, (T, k)),
+        _ptr(src_token, "src_token", torch.int32, (R,)),
+        _ptr(src_slot, "src_slot", torch.int32, (R,)),
+        _ptr(offsets, "offsets", torch.int32, (desc.E + 1,)),
+        _ptr(send_buf, "send_buf", dt, (P, d)),
+        _ptr(pair_dest, "pair_dest", torch.int32, (T, k)),
+        _ptr(pair_token, "pair_token", torch.int32, (P,)),
+        _ptr(pair_splits, "pair_splits", torch.int64, (desc.ep_size,)),
+        _ptr(pair_displs, "pair_displs", torch.int64, (desc.ep_size,)),
+        _ptr(recv_rows, "recv_rows", torch.int32, (R,)), wsp, wsn, _stream(stream)),
+        "moe_pack_dedup")
 
 
 def unpermute_combine(desc, y_perm, topk_idx, topk_gate, dest, y, stream=None):

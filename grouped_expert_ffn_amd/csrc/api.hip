@@ -12,6 +12,12 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static size_t elt_bytes(int dtype) { return dtype == MOE_DTYPE_BF16 ? 2 : 4; }
 
+// rows of a deduplicated send buffer: one per (destination rank, token) pair
+static int64_t max_pairs(const moe_layer_desc_t& d) {
+  return d.T * (int64_t)std::min(d.k, d.ep_size);
+}
+static size_t dedup_scratch_ints(const moe_layer_desc_t& d);
+
 Workspace workspace_layout(const moe_layer_desc_t& d) {
   Workspace w{};
   size_t off = 0;
@@ -24,8 +30,32 @@ Workspace workspace_layout(const moe_layer_desc_t& d) {
   off += align256((size_t)(gemm_max_mtiles(d) + 1) * sizeof(int4));
   w.act = off;
   off += align256((size_t)d.max_rows * d.d_ff * elt_bytes(d.dtype));
+  w.dedup = off;
+  off += align256(dedup_scratch_ints(d) * 4);
   w.total = off;
   return w;
+}
+
+// int32 entries of the deduplicated packing's scratch: pid and first_row
+// [T,k], pair_slot [max pairs], counts [E], offsets [E+1], flags [1]
+static size_t dedup_scratch_ints(const moe_layer_desc_t& d) {
+  const size_t tk = (size_t)d.T * d.k;
+  return 2 * tk + (size_t)max_pairs(d) + 2 * (size_t)d.E + 2;
+}
+
+static DedupScratch dedup_scratch(const moe_layer_desc_t& d, char* ws) {
+  const Workspace w = workspace_layout(d);
+  int32_t* p = reinterpret_cast<int32_t*>(ws + w.dedup);
+  const size_t tk = (size_t)d.T * d.k;
+  DedupScratch s;
+  s.tile_hist = reinterpret_cast<int32_t*>(ws + w.tile_hist);
+  s.pid = p;
+  s.first_row = p + tk;
+  s.pair_slot = p + 2 * tk;
+  s.counts = s.pair_slot + max_pairs(d);
+  s.offsets = s.counts + d.E;
+  s.flags = reinterpret_cast<uint32_t*>(s.offsets + d.E + 1);
+  return s;
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -134,8 +164,9 @@ static moe_status_t do_ffn(const moe_layer_desc_t& d, const void* x, const int32
 }
 
 // gathered bf16 rows are addressed with 32-bit byte offsets from h
+// (h: token rows [T,d], or a deduplicated send buffer of up to max_pairs rows)
 static moe_status_t check_gather(const moe_layer_desc_t& d) {
-  if (d.dtype == MOE_DTYPE_BF16 && d.T * (int64_t)d.d * 2 >= ((int64_t)1 << 32))
+  if (d.dtype == MOE_DTYPE_BF16 && max_pairs(d) * d.d * 2 >= ((int64_t)1 << 32))
     return MOE_ERR_SHAPE;
   return MOE_OK;
 }
@@ -240,6 +271,31 @@ MOE_EXPORT moe_status_t moe_grouped_ffn_gather(const moe_layer_desc_t* desc, con
                             {offsets, d.E + 1, false}}));
   MOE_TRY(check_ws(desc, ws, ws_bytes));
   return do_ffn(d, h, src_token, offsets, w1, w2, y_perm, (char*)ws, (hipStream_t)stream);
+}
+
+MOE_EXPORT moe_status_t moe_pack_dedup(const moe_layer_desc_t* desc, const void* h,
+                                       const int32_t* topk_idx, const int32_t* dest,
+                                       const int32_t* src_token, const int32_t* src_slot,
+                                       const int32_t* offsets, void* send_buf,
+                                       int32_t* pair_dest, int32_t* pair_token,
+                                       int64_t* pair_splits, int64_t* pair_displs,
+                                       int32_t* recv_rows, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_layer_desc_t& d = *desc;
+  const int64_t Tk = d.T * d.k, R = d.max_rows, P = max_pairs(d);
+  MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {topk_idx, Tk, false}, {dest, Tk, false},
+                            {src_token, R, false}, {src_slot, R, false},
+                            {offsets, d.E + 1, false}, {send_buf, P * d.d, true},
+                            {pair_dest, Tk, false}, {pair_token, P, false},
+                            {pair_splits, d.ep_size, false}, {pair_displs, d.ep_size, false},
+                            {recv_rows, R, false}}));
+  MOE_TRY(check_ws(desc, ws, ws_bytes));
+  HIP_TRY(launch_pack_dedup(h, topk_idx, dest, src_token, src_slot, offsets, send_buf, pair_dest,
+                            pair_token, pair_splits, pair_displs, recv_rows,
+                            dedup_scratch(d, (char*)ws), d.T, d.E, d.k, d.ep_size, d.ep_rank,
+                            d.max_rows, (int)(d.d * elt_bytes(d.dtype)), (hipStream_t)stream));
+  return MOE_OK;
 }
 
 MOE_EXPORT moe_status_t moe_unpermute_combine(const moe_layer_desc_t* desc, const void* y_perm,

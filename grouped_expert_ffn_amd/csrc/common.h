@@ -27,7 +27,20 @@ struct Workspace {
   size_t tile_hist;  // [n_tiles, E] int32 per-tile expert counts, then their prefixes
   size_t gemm_tiles; // [max_mtiles] int4 grouped-GEMM tile table + count
   size_t act;        // [max_rows, d_ff] dtype: SwiGLU/ReLU activations
+  size_t dedup;      // deduplicated packing: pid, first_row [T,k]; pair_slot [pairs];
+                     // counts [E], offsets [E+1], flags [1] (int32)
   size_t total;
+};
+
+// Scratch of the deduplicated packing, carved from the workspace.
+struct DedupScratch {
+  int32_t* tile_hist;
+  int32_t* pid;        // [T,k] rank of a token's first slot to that rank, else -1
+  int32_t* first_row;  // [T,k] pair row planned for those first slots
+  int32_t* pair_slot;  // [pairs] slot of each pair's first slot (plan by-product)
+  int32_t* counts;     // [ep_size] pairs per rank (plan by-product)
+  int32_t* offsets;    // [ep_size + 1]
+  uint32_t* flags;     // [1] the plan's flags on the pair table (not reported)
 };
 
 Workspace workspace_layout(const moe_layer_desc_t& d);
@@ -51,6 +64,13 @@ hipError_t launch_dispatch_plan(const int32_t* idx, int32_t* tile_hist, int32_t*
                                 int64_t max_rows, int ep_size, hipStream_t s);
 hipError_t launch_permute_rows(const void* h, const int32_t* dest, void* x_perm, int64_t T,
                                int k, int row_bytes, hipStream_t s);
+hipError_t launch_pack_dedup(const void* h, const int32_t* idx, const int32_t* dest,
+                             const int32_t* src_token, const int32_t* src_slot,
+                             const int32_t* offsets, void* send_buf, int32_t* pair_dest,
+                             int32_t* pair_token, int64_t* pair_splits, int64_t* pair_displs,
+                             int32_t* recv_rows, const DedupScratch& w, int64_t T, int E, int k,
+                             int ep_size, int ep_rank, int64_t max_rows, int row_bytes,
+                             hipStream_t s);
 hipError_t launch_combine(const void* y_perm, const int32_t* idx, const float* gate,
                           const int32_t* dest, void* y, int64_t T, int k, int d, int dtype,
                           int e_lo, int e_hi, hipStream_t s);

@@ -14,6 +14,8 @@
 // stable in-tile rank by wave ballots, then bandwidth-bound row copies. All
 // integer results are independent of scheduling (the only atomics are
 // integer counts and flag ORs).
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -458,6 +460,104 @@ hipError_t launch_permute_rows(const void* h, const int32_t* dest, void* x_perm,
                        (const float*)h, dest, (float*)x_perm, T, k, row_bytes / 4);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 4'. Expert-parallel packing with token deduplication: one send row per
+//     (destination rank, token) pair. The pairs are planned by the dispatch
+//     plan itself, run on a table that keeps, per token, only the first sent
+//     slot for each rank (its "expert" id is the rank); the row copy then
+//     writes each pair's row once.
+
+// pid[t,j] = rank of slot j if it is sent (dest >= 0) and no earlier slot of
+// token t goes to the same rank; -1 otherwise.
+__global__ __launch_bounds__(256) void pair_ids_kernel(const int32_t* __restrict__ idx,
+                                                       const int32_t* __restrict__ dest,
+                                                       int32_t* __restrict__ pid, int64_t T,
+                                                       int k, int el) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int rk[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j >= k) break;
+    const int64_t a = t * k + j;
+    const int r = dest[a] >= 0 ? idx[a] / el : -1;
+    bool first = r >= 0;
+#pragma unroll
+    for (int i = 0; i < j; ++i) first = first && rk[i] != r;
+    rk[j] = r;
+    pid[a] = first ? r : -1;
+  }
+}
+
+// pair_dest[t,j] = the pair row of slot j's rank (the row planned for the
+// token's first slot to that rank), -1 for unsent slots.
+__global__ __launch_bounds__(256) void pair_dest_kernel(const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ dest,
+                                                        const int32_t* __restrict__ first_row,
+                                                        int32_t* __restrict__ pair_dest,
+                                                        int64_t T, int k, int el) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  for (int j = 0; j < k; ++j) {
+    const int64_t a = t * k + j;
+    int32_t row = -1;
+    if (dest[a] >= 0) {
+      const int r = idx[a] / el;
+      for (int i = 0; i <= j; ++i) {
+        const int64_t b = t * k + i;
+        if (dest[b] >= 0 && idx[b] / el == r) {
+          row = first_row[b];
+          break;
+        }
+      }
+    }
+    pair_dest[a] = row;
+  }
+}
+
+// recv_rows[i] = pair row holding the token of grouped row i, for the local
+// experts' rows offsets[e_lo] .. min(offsets[e_hi], max_rows) - 1.
+__global__ __launch_bounds__(256) void recv_rows_kernel(const int32_t* __restrict__ offsets,
+                                                        int e_lo, int e_hi, int64_t max_rows,
+                                                        const int32_t* __restrict__ src_token,
+                                                        const int32_t* __restrict__ src_slot,
+                                                        const int32_t* __restrict__ pair_dest,
+                                                        int32_t* __restrict__ recv_rows, int k) {
+  const int64_t lo = min((int64_t)offsets[e_lo], max_rows);
+  const int64_t hi = min((int64_t)offsets[e_hi], max_rows);
+  for (int64_t i = lo + (int64_t)blockIdx.x * 256 + threadIdx.x; i < hi;
+       i += (int64_t)gridDim.x * 256)
+    recv_rows[i] = pair_dest[(int64_t)src_token[i] * k + src_slot[i]];
+}
+
+hipError_t launch_pack_dedup(const void* h, const int32_t* idx, const int32_t* dest,
+                             const int32_t* src_token, const int32_t* src_slot,
+                             const int32_t* offsets, void* send_buf, int32_t* pair_dest,
+                             int32_t* pair_token, int64_t* pair_splits, int64_t* pair_displs,
+                             int32_t* recv_rows, const DedupScratch& w, int64_t T, int E, int k,
+                             int ep_size, int ep_rank, int64_t max_rows, int row_bytes,
+                             hipStream_t s) {
+  const int el = E / ep_size;
+  const unsigned tb = (unsigned)((T + 255) / 256);
+  const int64_t max_pairs = T * (int64_t)min(k, ep_size);
+  if (T > 0)
+    hipLaunchKernelGGL(pair_ids_kernel, dim3(tb), dim3(256), 0, s, idx, dest, w.pid, T, k, el);
+  hipError_t err = launch_dispatch_plan(w.pid, w.tile_hist, w.counts, w.offsets, w.first_row,
+                                        pair_token, w.pair_slot, pair_splits, pair_displs,
+                                        w.flags, T, ep_size, k, -1, max_pairs, ep_size, s);
+  if (err != hipSuccess) return err;
+  if (T > 0)
+    hipLaunchKernelGGL(pair_dest_kernel, dim3(tb), dim3(256), 0, s, idx, dest, w.first_row,
+                       pair_dest, T, k, el);
+  if (max_rows > 0) {
+    const unsigned rb = (unsigned)std::min<int64_t>((max_rows + 255) / 256, 1024);
+    hipLaunchKernelGGL(recv_rows_kernel, dim3(rb), dim3(256), 0, s, offsets, ep_rank * el,
+                       (ep_rank + 1) * el, max_rows, src_token, src_slot, pair_dest, recv_rows,
+                       k);
+  }
+  return launch_permute_rows(h, w.first_row, send_buf, T, k, row_bytes, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -167,15 +167,40 @@ moe_status_t moe_grouped_ffn(const moe_layer_desc_t* desc, const void* x_perm,
 /* The same grouped expert FFN with dispatch fused into the first GEMM: row r
  * of an expert's group is read straight from h [T,d] at token src_token[r]
  * (the inverse map moe_permute writes), so the rows are never copied into
- * x_perm. "Dropless MoE Is a Runtime Problem as Much as a Model Design",
+ * x_perm. h may also be a deduplicated send buffer from moe_pack_dedup,
+ * with its recv_rows in place of src_token. "Dropless MoE Is a Runtime Problem as Much as a Model Design",
  * expert-parallelism paragraph: fusing dispatch into the expert computation
  * removes an intermediate write and its read. Results are bit-identical to
- * moe_grouped_ffn on x_perm. bf16 needs T*d*2 bytes below 4 GiB
- * (MOE_ERR_SHAPE otherwise). */
+ * moe_grouped_ffn on x_perm. bf16 needs T*min(k,ep_size)*d*2 bytes below
+ * 4 GiB (MOE_ERR_SHAPE otherwise). */
 moe_status_t moe_grouped_ffn_gather(const moe_layer_desc_t* desc, const void* h,
                                     const int32_t* src_token, const int32_t* offsets,
                                     const void* w1, const void* w2, void* y_perm, void* ws,
                                     size_t ws_bytes, void* stream);
+
+/* Expert-parallel packing with token deduplication: one send row per
+ * (destination rank, token) pair instead of one per (token, slot).
+ * "Dropless MoE Is a Runtime Problem as Much as a Model Design",
+ * expert-parallelism paragraph: a token routed to several experts on one
+ * destination needs to cross the network once. Inputs are the routing and
+ * the plan of moe_permute (x_perm may have been NULL there): a slot is sent
+ * when dest >= 0, to rank topk_idx / (E / ep_size).
+ *   send_buf    [T*min(k,ep_size), d] pair rows, ordered by rank then token;
+ *               rows past the pair count are untouched
+ *   pair_dest   [T,k] send row of each slot's pair, -1 for unsent slots
+ *   pair_token  [T*min(k,ep_size)] token of each pair row
+ *   pair_splits, pair_displs [ep_size] rows and first row of each rank
+ *   recv_rows   [max_rows] for this rank's grouped rows offsets[e_lo]..
+ *               min(offsets[e_hi], max_rows)-1: the send row holding that
+ *               row's token, so moe_grouped_ffn_gather(desc, send_buf,
+ *               recv_rows, ...) runs the local experts on the deduplicated rows
+ * Bit-exact and independent of launch timing. Needs the workspace of desc. */
+moe_status_t moe_pack_dedup(const moe_layer_desc_t* desc, const void* h, const int32_t* topk_idx,
+                            const int32_t* dest, const int32_t* src_token,
+                            const int32_t* src_slot, const int32_t* offsets, void* send_buf,
+                            int32_t* pair_dest, int32_t* pair_token, int64_t* pair_splits,
+                            int64_t* pair_displs, int32_t* recv_rows, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /* Unpermute + combine: y[t] = sum_j topk_gate[t,j] * y_perm[dest[t,j]] over
  * slots with dest >= 0 whose expert is local, summed in float32 in slot
