@@ -47,23 +47,21 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
+// One tile-table entry (uniform), read with a scalar load. The persistent
+// loops look it up right after a slice barrier or after an epilogue, where
+// no LDS read is outstanding, so waiting for the scalar load costs only its
+// own latency; a vector load would also wait for every slice load in flight.
+__device__ __forceinline__ int4 tile_entry(const int4* __restrict__ tiles, int mt) {
+  using CInt = const __attribute__((address_space(4))) int;
+  CInt* p = (CInt*)tiles + 4 * mt;
+  return make_int4(p[0], p[1], p[2], 0);
+}
+
 // Tiles that do not fill a whole round of the persistent grid: when they
 // would occupy at most half of it, the main kernel stops after the whole
 // rounds and a second launch runs each leftover tile as two half-height
 // tiles, which keeps more CUs busy. Splitting by rows leaves every output's
 // K accumulation order unchanged, so results do not depend on the split.
-// One tile-table entry, read with a vector load and made uniform again. A
-// scalar load would share the lgkm counter with the GEMM's LDS reads; with
-// both kinds pending the compiler can only wait for the counter to drain,
-// not for the oldest LDS reads.
-__device__ __forceinline__ int4 tile_entry(const int4* __restrict__ tiles, int mt) {
-  int mv;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(mv) : "s"(mt));
-  const int4 e = tiles[mv];
-  return make_int4(__builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
-                   __builtin_amdgcn_readfirstlane(e.z), 0);
-}
-
 __device__ __forceinline__ int main_tile_end(int total, int G) {
   const int full = total / G * G;
   const int tail = total - full;

@@ -4,8 +4,8 @@
 //
 // Both operands are K-contiguous, the natural layout for the bf16 MFMAs:
 // every lane feeds 8 consecutive K values of one row of each operand. K
-// slices of A and B stream from global memory straight into LDS
-// (global_load_lds_dwordx4), double-buffered. Each LDS row holds 16-byte
+// slices of A and B stream from global memory straight into LDS (buffer or
+// global loads with the LDS bit, 16 bytes per lane), double-buffered. Each LDS row holds 16-byte
 // chunks stored at chunk ^ (row-dependent key), so the 16 rows one fragment
 // read touches fall in distinct banks of the 256-byte-wide LDS.
 //
@@ -29,7 +29,7 @@ __device__ __forceinline__ float silu_f(float g) {
 
 // ---------------------------------------------------------------------------
 // The tile: K slices of A and B go from global memory straight into LDS
-// (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16 *
+// (loads with the LDS bit: each lane's 16 bytes land at LDS base + 16 *
 // lane), so no VGPRs or ds_write instructions are spent on staging; two
 // slices are kept in LDS, the next one in flight while one is multiplied.
 // One such load fills 1 KiB of consecutive LDS rows; the XOR swizzle of the
@@ -44,8 +44,8 @@ struct SliceLayout {
 
 // Workgroup barrier that orders LDS traffic only: this wave's LDS reads and
 // writes are complete, then all waves meet. Unlike __syncthreads() it does not
-// drain outstanding global loads, so slices prefetched into LDS by
-// global_load_lds stay in flight across it (their completion is awaited
+// drain outstanding global loads, so slices prefetched into LDS by the
+// direct loads stay in flight across it (their completion is awaited
 // explicitly with wait_vmcnt before the barrier that publishes them).
 // The lgkmcnt wait goes through the builtin so the compiler's own wait
 // insertion knows that every earlier LDS read has returned; the barrier itself
@@ -166,11 +166,37 @@ struct TileGemmDL {
         off[i] = ((uint32_t)row * (uint32_t)K + (uint32_t)(c * 8)) * 2u;
       }
     };
-    // a scalar base plus a 32-bit per-lane byte offset: the load's saddr form,
-    // one VGPR per load instead of a 64-bit address
+    // When a wave's loads are all token rows or all weight rows (RPL * LPW
+    // divides BM), they go through one buffer resource per slice: base = the
+    // tile's a or b pointer, slice offset in the scalar offset, 32-bit lane
+    // offset in the VGPR, LDS destination in M0 (buffer_load_dwordx4 ... lds).
+    // Buffer loads rather than global_load_lds because the compiler's wait
+    // insertion treats a global load into LDS as an access that may hit both
+    // counters and then turns every LDS-read wait into a full drain while one
+    // is outstanding; with buffer loads its LDS-read waits stay exact.
+    // Resource word 3 = 0x00020000 (32-bit data format, the raw-buffer setting
+    // of this GPU family); the record count is the maximum, so no clamping.
+    constexpr bool WAVE_UNIFORM = BM % (LPW * L::RPL) == 0;
+    const bool wave_a = wave * LPW * L::RPL < BM;
+    // otherwise: a scalar base plus a 32-bit per-lane byte offset (the
+    // global load's saddr form), one VGPR per load
     auto issue = [&](const GemmTile& t, int kt, int buf) {
       bf16* base = lds + buf * LDS_BUF + wave * LPW * L::RPL * BK;
       const uint32_t ko = (uint32_t)kt * (BK * 2);
+      if constexpr (WAVE_UNIFORM) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16*>(wave_a ? t.a : t.b), (short)0, -1, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+          uint32_t o = off[i];
+          if (GA && wave_a)
+            o = o * (uint32_t)(K * 2) + (((wave * LPW + i) & 1) ? chunk_odd : chunk_even);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)(base + i * L::RPL * BK), 16, o, ko, 0,
+              0);
+        }
+        return;
+      }
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         uint32_t o = off[i];
