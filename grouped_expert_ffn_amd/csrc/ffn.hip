@@ -110,7 +110,11 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ rows, const bf16* __restrict__ W,
     bf16* __restrict__ C, const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr,
     int N, int K, int64_t w_stride, int n_n, int64_t ldc, int G) {
-  using TG = TileGemmDL<HM, BN, WM, WN, EPI, BK, MF, GA>;
+  // one tile per workgroup and half the MFMAs per slice: a third slice
+  // buffer (when it fits in the 160 KiB of LDS) keeps two slices in flight
+  using TG3 = TileGemmDL<HM, BN, WM, WN, EPI, BK, MF, GA, 3>;
+  using TG = typename std::conditional<TG3::LDS_ELEMS * 2 <= 160 * 1024, TG3,
+                                       TileGemmDL<HM, BN, WM, WN, EPI, BK, MF, GA, 2>>::type;
   __shared__ __attribute__((aligned(1024))) bf16 lds[TG::LDS_ELEMS];
   const int n_m = *n_mt_ptr;
   const int total = n_m * n_n;

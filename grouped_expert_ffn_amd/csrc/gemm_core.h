@@ -80,7 +80,8 @@ struct GemmTile {
 // two LDS buffers as one sequence that runs across tile boundaries: the next
 // tile's first slices are already in flight while the current tile's
 // epilogue converts and stores its accumulators.
-template <int BM, int BN, int WM, int WN, int EPI, int BK = 64, int MF = 16, bool GA = false>
+template <int BM, int BN, int WM, int WN, int EPI, int BK = 64, int MF = 16, bool GA = false,
+          int NBUF = 2>
 struct TileGemmDL {
   using L = SliceLayout<BK>;
   static constexpr int NT = 64 * WM * WN;
@@ -93,7 +94,7 @@ struct TileGemmDL {
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int TM = WTM / MF, TN = WTN / MF;   // MFMA tiles per wave
   static constexpr int LDS_BUF = ROWS * BK;
-  static constexpr int LDS_ELEMS = 2 * LDS_BUF;
+  static constexpr int LDS_ELEMS = NBUF * LDS_BUF;
   using Acc = typename std::conditional<MF == 32, f32x16, f32x4>::type;
   static constexpr int NACC = MF == 32 ? 16 : 4;
   static constexpr int KSUB = MF == 32 ? 16 : 32;  // K per MFMA
@@ -101,6 +102,7 @@ struct TileGemmDL {
   static constexpr int NSUB = BK / KSUB;           // sub-steps per slice
   static constexpr int TU = GATED ? TN : 1;
   static_assert(MF == 16 || MF == 32, "MFMA shape");
+  static_assert(NBUF == 2 || NBUF == 3, "two or three slice buffers");
   static_assert(LOADS % NW == 0, "loads must split evenly over waves");
   static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be a multiple of the MFMA tile");
   static_assert(BK % 32 == 0 && NSUB >= 2, "two or more MFMA sub-steps per K slice");
@@ -213,9 +215,14 @@ struct TileGemmDL {
     if (!l_live) return;
     GemmTile ct = lt;   // tile being multiplied
     set_offsets(lt);
-    auto issue_next = [&](int buf) {
+    // the buffer the next slice goes to; whether the latest call issued loads
+    int l_buf = 0;
+    bool l_issued = false;
+    auto issue_next = [&]() {
+      l_issued = l_live;
       if (!l_live) return;
-      issue(lt, l_k, buf);
+      issue(lt, l_k, l_buf);
+      l_buf = l_buf + 1 == NBUF ? 0 : l_buf + 1;
       if (++l_k == lt.nk) {
         l_k = 0;
         l_live = get(++l_idx, lt);
@@ -351,56 +358,70 @@ struct TileGemmDL {
       }
     };
 
-    // ---- the tile and slice loops. Global slice g sits in LDS buffer g & 1.
-    // Fragment reads are software-pipelined across the slice barrier:
-    // sub-step 1 is read while sub-step 0 is multiplied, and sub-step 0 of
-    // slice g+1 is read right after the barrier that publishes it, while
-    // sub-step 1 of slice g is multiplied. Slice g+2 is fetched into the buffer slice g
-    // just left, so it has a whole slice of MFMAs to arrive. sched_barrier
-    // fences keep the compiler from moving MFMAs across the slice barrier,
-    // which would leave the reads before it uncovered.
+    // ---- the tile and slice loops. Global slice g sits in LDS buffer
+    // g % NBUF. Fragment reads are software-pipelined across the slice
+    // barrier: sub-step 1 is read while sub-step 0 is multiplied, and sub-step
+    // 0 of slice g+1 is read right after the barrier that publishes it, while
+    // sub-step 1 of slice g is multiplied. Slice g+NBUF is fetched into the
+    // buffer slice g just left, so it has NBUF-1 slices of MFMAs to arrive.
+    // sched_barrier fences keep the compiler from moving MFMAs across the
+    // slice barrier, which would leave the reads before it uncovered.
     static_assert(NSUB == 2, "the loop below pipelines two sub-steps per slice");
     using Yes = std::integral_constant<bool, true>;
     using No = std::integral_constant<bool, false>;
-    issue_next(0);
-    wait_vmcnt<0>();
+    // Wait until the slice that the next barrier publishes has landed: with
+    // three buffers the latest slice's loads may stay in flight. Only loads
+    // are outstanding at these waits (the epilogue's stores are drained at
+    // the first barrier of the next tile), and loads complete in order.
+    auto wait_slice = [&]() {
+      if (NBUF == 3 && l_issued)
+        wait_vmcnt<LPW>();
+      else
+        wait_vmcnt<0>();
+    };
+    auto next_buf = [](int b) { return b + 1 == NBUF ? 0 : b + 1; };
+    issue_next();
+    if (NBUF == 3) issue_next();
+    wait_slice();
     lds_barrier();
-    issue_next(1);
+    issue_next();
     FragsB b0, b1;
-    int g = 0;   // global slice index of this workgroup
+    int cb = 0;   // LDS buffer of the slice being multiplied
     // The slice loop is rotated so that its head follows a slice barrier,
     // where no LDS read is outstanding: the compiler's wait insertion is
     // exact inside a loop body but waits for everything at a loop head that
     // outstanding reads reach through the back edge.
     for (int c_idx = 0;; ++c_idx) {
-      // the tile's first slice is in LDS buffer g & 1
+      // the tile's first slice is in LDS buffer cb
       zero_acc();
-      read_b(g & 1, 0, b0);
+      read_b(cb, 0, b0);
 #pragma unroll
-      for (int y = 0; y < TM; ++y) fy[y] = read_a(g & 1, 0, y);
-      step(Yes{}, b0, b1, g & 1, 1);
+      for (int y = 0; y < TM; ++y) fy[y] = read_a(cb, 0, y);
+      step(Yes{}, b0, b1, cb, 1);
       __builtin_amdgcn_sched_barrier(0);
-      // slice g fully read by this wave; slice g+1 landed from this wave
+      // slice g fully read by this wave; slice g+1 landed from this wave (and
+      // the previous tile's stores drained)
       wait_vmcnt<0>();
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      for (int ck = 0; ck < ct.nk - 1; ++ck, ++g) {
-        const int buf = g & 1;
-        issue_next(buf);                       // slice g+2 into the buffer g left
-        step(Yes{}, b1, b0, buf ^ 1, 0);       // last sub-step of g, reads g+1
+      for (int ck = 0; ck < ct.nk - 1; ++ck) {
+        const int nb = next_buf(cb);
+        issue_next();                          // slice g+NBUF into the buffer g left
+        step(Yes{}, b1, b0, nb, 0);            // last sub-step of g, reads g+1
         __builtin_amdgcn_sched_barrier(0);
-        step(Yes{}, b0, b1, buf ^ 1, 1);       // sub-step 0 of g+1, reads its sub-step 1
+        step(Yes{}, b0, b1, nb, 1);            // sub-step 0 of g+1, reads its sub-step 1
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<0>();                       // slice g+2 landed from this wave ...
+        wait_slice();                          // slice g+2 landed from this wave ...
         lds_barrier();                         // ... and slice g+1 read by every wave
         __builtin_amdgcn_sched_barrier(0);
+        cb = nb;
       }
       // the tile's last slice; its epilogue runs while the next tile's first
       // slices load, and that tile's first fragments are read after it
-      issue_next(g & 1);
+      issue_next();
       step(No{}, b1, b0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      ++g;
+      cb = next_buf(cb);
       epilogue(ct);
       // the load cursor has already looked up the tile after this one
       if (c_idx + 1 >= tiles_end) break;
