@@ -59,9 +59,9 @@ __device__ __forceinline__ int4 tile_entry(const int4* __restrict__ tiles, int m
 
 // Tiles that do not fill a whole round of the persistent grid: when they
 // would occupy at most half of it, the main kernel stops after the whole
-// rounds and a second launch runs each leftover tile as two half-height
-// tiles, which keeps more CUs busy. Splitting by rows leaves every output's
-// K accumulation order unchanged, so results do not depend on the split.
+// rounds and a second launch runs each leftover tile cut into 2, 4 or 8
+// pieces, which keeps more CUs busy. Cutting by rows and columns leaves every
+// output's K accumulation order unchanged, so results do not depend on it.
 __device__ __forceinline__ int main_tile_end(int total, int G) {
   const int full = total / G * G;
   const int tail = total - full;
@@ -102,47 +102,76 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
   TG::run_tiles(get, N, K, C, ldc, lds);
 }
 
-// The leftover tiles of the kernel above (same tile table, same order), as
-// half-height tiles of HM = BM / 2 rows: unit u is half u & 1 of tile
-// main_tile_end + u / 2. G is the main kernel's grid size.
-template <int HM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA>
+// The leftover tiles of the kernel above (same tile table, same order),
+// each cut into S = SM * SN pieces of BM / SM rows by BN / SN columns: unit
+// u is piece u % S of tile main_tile_end + u / S. One piece per workgroup;
+// fewer MFMAs per K slice than a whole tile, so the piece loop keeps three
+// slice buffers when they fit in the 160 KiB of LDS.
+template <int SM, int SN, int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF,
+          bool GA>
+struct TailPieces {
+  static constexpr int HM = BM / SM, HN = BN / SN, S = SM * SN;
+  using TG3 = TileGemmDL<HM, HN, WM, WN, EPI, BK, MF, GA, 3>;
+  using TG = typename std::conditional<TG3::LDS_ELEMS * 2 <= 160 * 1024, TG3,
+                                       TileGemmDL<HM, HN, WM, WN, EPI, BK, MF, GA, 2>>::type;
+  __device__ static void run(const bf16* A, const int32_t* rows, const bf16* W, bf16* C,
+                             const int4* tiles, int n_m, int first, int left, int N, int K,
+                             int64_t w_stride, int n_n, int64_t ldc, bf16* lds) {
+    const int units = S * left;
+    const int nk = K / BK;
+    const int slot = xcd_virtual_id(blockIdx.x, gridDim.x, 0);
+    auto get = [&](int i, GemmTile& t) -> bool {
+      // units <= gridDim.x; pieces that fall entirely past the tile's rows
+      // or the weight's columns are skipped
+      for (int u = slot + i * (int)gridDim.x; u < units; u += gridDim.x) {
+        int mt, nt;
+        tile_coords<GROUP_M>(first + u / S, n_m, n_n, mt, nt);
+        const int part = u % S;
+        const int4 e = tile_entry(tiles, mt);
+        const int ex = e.x, ey = e.y + (part % SM) * HM, ez = e.z;
+        if (ey >= ez) continue;
+        const int n0 = nt * BN + (part / SM) * HN;
+        if (n0 >= N) continue;
+        t.a = GA ? A : A + (int64_t)ey * K;
+        t.rows = GA ? rows + ey : nullptr;
+        t.a_rows = min(ez - ey, HM);
+        t.n0 = n0;
+        t.b = W + (int64_t)ex * w_stride + (int64_t)n0 * K;
+        t.c_row = ey;
+        t.nk = nk;
+        return true;
+      }
+      return false;
+    };
+    TG::run_tiles(get, N, K, C, ldc, lds);
+  }
+};
+
+// The leftover tiles with the finest split S in {2, 4, 8} for which
+// S * leftover <= G (G: the main kernel's grid size, also this grid's).
+// Splitting by rows and columns leaves every output's K order unchanged.
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ rows, const bf16* __restrict__ W,
     bf16* __restrict__ C, const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr,
     int N, int K, int64_t w_stride, int n_n, int64_t ldc, int G) {
-  // one tile per workgroup and half the MFMAs per slice: a third slice
-  // buffer (when it fits in the 160 KiB of LDS) keeps two slices in flight
-  using TG3 = TileGemmDL<HM, BN, WM, WN, EPI, BK, MF, GA, 3>;
-  using TG = typename std::conditional<TG3::LDS_ELEMS * 2 <= 160 * 1024, TG3,
-                                       TileGemmDL<HM, BN, WM, WN, EPI, BK, MF, GA, 2>>::type;
-  __shared__ __attribute__((aligned(1024))) bf16 lds[TG::LDS_ELEMS];
+  using P2 = TailPieces<2, 1, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
+  using P4 = TailPieces<2, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
+  using P8 = TailPieces<4, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
+  constexpr int E2 = P2::TG::LDS_ELEMS, E4 = P4::TG::LDS_ELEMS, E8 = P8::TG::LDS_ELEMS;
+  constexpr int ELEMS = E2 > E4 ? (E2 > E8 ? E2 : E8) : (E4 > E8 ? E4 : E8);
+  __shared__ __attribute__((aligned(1024))) bf16 lds[ELEMS];
   const int n_m = *n_mt_ptr;
   const int total = n_m * n_n;
   const int first = main_tile_end(total, G);
-  const int units = 2 * (total - first);
-  const int nk = K / BK;
-  const int slot = xcd_virtual_id(blockIdx.x, gridDim.x, 0);
-  auto get = [&](int i, GemmTile& t) -> bool {
-    // one unit per workgroup at most (units <= G); an empty lower half
-    // (a tile of HM rows or fewer) is skipped
-    for (int u = slot + i * (int)gridDim.x; u < units; u += gridDim.x) {
-      int mt, nt;
-      tile_coords<GROUP_M>(first + u / 2, n_m, n_n, mt, nt);
-      const int4 e = tile_entry(tiles, mt);
-      const int ex = e.x, ey = e.y + (u & 1) * HM, ez = e.z;
-      if (ey >= ez) continue;
-      t.a = GA ? A : A + (int64_t)ey * K;
-      t.rows = GA ? rows + ey : nullptr;
-      t.a_rows = min(ez - ey, HM);
-      t.n0 = nt * BN;
-      t.b = W + (int64_t)ex * w_stride + (int64_t)t.n0 * K;
-      t.c_row = ey;
-      t.nk = nk;
-      return true;
-    }
-    return false;
-  };
-  TG::run_tiles(get, N, K, C, ldc, lds);
+  const int left = total - first;
+  if (left == 0) return;
+  if (8 * left <= G)
+    P8::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, lds);
+  else if (4 * left <= G)
+    P4::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, lds);
+  else
+    P2::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, lds);
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA = false>
@@ -159,7 +188,7 @@ static hipError_t grouped_gemm_dl_launch(const bf16* A, const int32_t* rows, con
                      K, w_stride, n_n, ldc);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((grouped_gemm_tail_kernel<BM / 2, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>),
+  hipLaunchKernelGGL((grouped_gemm_tail_kernel<BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>),
                      dim3((unsigned)G), dim3(64 * WM * WN), 0, s, A, rows, W, C, tiles, n_mt, N,
                      K, w_stride, n_n, ldc, (int)G);
   return hipGetLastError();
