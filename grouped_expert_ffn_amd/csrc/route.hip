@@ -105,11 +105,13 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void router_skinny_kernel(
 }
 
 // E >= 64: the direct-load MFMA tile with a float epilogue (bias added there).
+// A router tile has few MFMAs per K slice (BN = E_pad columns at most), so
+// three slice buffers keep two slices in flight.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void router_tile_kernel(
     const bf16* __restrict__ h, const bf16* __restrict__ wt, const float* __restrict__ bias,
     float* __restrict__ logits, int64_t T, int d, int E, int E_pad, int n_m, int n_n) {
-  using TG = TileGemmDL<BM, BN, WM, WN, EPI_ROUTER_F32, 64, 16>;
+  using TG = TileGemmDL<BM, BN, WM, WN, EPI_ROUTER_F32, 64, 16, false, 3>;
   __shared__ __attribute__((aligned(1024))) bf16 lds[TG::LDS_ELEMS];
   const int total = n_m * n_n;
   const int G = gridDim.x;
