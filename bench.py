@@ -78,6 +78,27 @@ def measured_traffic(workload):
     return float(m_b.group(1))
 
 
+def host_description():
+    """CPU model and the BLAS numpy links, for the CPU baseline's record."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+                if i.get("user_api") == "blas"]
+        blas = ", ".join(libs) or None
+    except Exception:  # pragma: no cover
+        pass
+    return model, blas
+
+
 def cpu_baseline(cfg, inp, capacity, sample_tokens, min_seconds):
     """The oracle, untouched, on the first `sample_tokens` tokens of the same
     workload (all expert weights), timed on the host cores; the sample is
@@ -99,8 +120,9 @@ def cpu_baseline(cfg, inp, capacity, sample_tokens, min_seconds):
                 ep_rank=cfg.ep_rank)
         total += time.perf_counter() - t0
         runs += 1
+    model, blas = host_description()
     return {"value": Ts * runs / total, "unit": "routed tokens/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "blas": blas,
             "sample": f"first {Ts} of {cfg.T} tokens of {cfg.name}, all expert weights, "
                       f"float64 numpy oracle, {runs} run(s) in {total:.1f} s"}
 
@@ -256,6 +278,24 @@ def dedup_bench(G, desc, h, b, w1, w2, ws, reps=10):
         "pack_GBs": pack_bytes / (info["pack_dedup_ms"] / 1e3) / 1e9,
         "ffn_rows_bitwise_equal": bool(torch.equal(y2[lo:hi], b.y_perm[lo:hi]))})
     return info
+
+
+def routing_report(cfg, b, capacity, eb):
+    """The step's routing population: assignments per expert, rows kept and
+    dropped per expert (capacity mode), and for an expert-parallel share the
+    rows, payload bytes and message count of each destination's segment."""
+    counts = b.counts.cpu().numpy().astype(np.int64)
+    kept = counts if capacity < 0 else np.minimum(counts, capacity)
+    rep = {"counts_per_expert": counts.tolist(), "kept_per_expert": kept.tolist(),
+           "dropped_per_expert": (counts - kept).tolist(), "dropped": int((counts - kept).sum()),
+           "empty_experts": int((counts == 0).sum())}
+    if cfg.ep_size > 1:
+        splits = b.send_splits.cpu().numpy().astype(np.int64)
+        remote = [r for r in range(cfg.ep_size) if r != cfg.ep_rank]
+        rep["send_rows_per_rank"] = splits.tolist()
+        rep["payload_bytes_per_remote_rank"] = [int(splits[r]) * cfg.d * eb for r in remote]
+        rep["messages"] = int(sum(1 for r in remote if splits[r] > 0))
+    return rep
 
 
 def main():
@@ -417,6 +457,7 @@ def main():
                 (permute_bytes + combine_bytes) / ((st_ms[1] + st_ms[3]) / 1e3) / 1e9 / HBM_PEAK_GBS,
             "rows_kept": n_kept, "rows_local": n_local, "flags": flags,
         },
+        "routing": routing_report(cfg, b, capacity, eb),
         "cold_mall": cold,
         "env": {"device": torch.cuda.get_device_name(), "torch": torch.__version__,
                 "hip": torch.version.hip, "library_sha": library_sha()},
