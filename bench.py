@@ -13,7 +13,7 @@ two MFMA GEMMs), per-stage figures, and the CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--skip-cpu-baseline]
-                    [--cold-steps N] [--gather] [--ablation] [--dedup]
+                    [--cold-steps N] [--gather] [--slots] [--ablation] [--dedup]
 
 After the timed steps, N more steps run one by one, each after a 512 MiB
 write that evicts the 256 MiB last-level cache (MALL); their event-timed
@@ -311,6 +311,10 @@ def main():
     ap.add_argument("--gather", action="store_true",
                     help="fused dispatch: permute makes only the plan and the first expert GEMM "
                          "reads token rows from h through src_token")
+    ap.add_argument("--slots", action="store_true",
+                    help="fused dispatch and slot-ordered output: permute makes only the plan, "
+                         "the first expert GEMM gathers token rows from h, the second writes "
+                         "each row to its (token, slot) row, and combine reads those")
     ap.add_argument("--ablation", action="store_true",
                     help="also time the grouped FFN beside a launch per expert and the padded "
                          "capacity layout, with the same kernels on the same plan")
@@ -323,6 +327,8 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
+    if args.dedup and args.slots:
+        ap.error("--dedup compares with the step's y_perm, which --slots does not write")
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
               "expert-parallel exchange across GPUs is not part of it", file=sys.stderr)
@@ -353,8 +359,10 @@ def main():
     h, wr = dev(inp["h"]), dev(inp["w_router"])
     bias = None if inp["bias"] is None else dev(inp["bias"], torch.float32)
     w1, w2 = dev(inp["w1"]), dev(inp["w2"])
-    gather = args.gather
+    slots = args.slots
+    gather = args.gather or slots
     b = G.alloc_buffers(desc, x_perm=not gather)
+    y_slots = (torch.empty((cfg.T * cfg.k, cfg.d), dtype=dt, device="cuda") if slots else None)
     ws = G.alloc_workspace(desc)
     y = torch.empty((cfg.T, cfg.d), dtype=dt, device="cuda")
     stream = torch.cuda.current_stream()
@@ -369,13 +377,18 @@ def main():
                   b.src_slot, b.send_splits, b.send_displs, b.flags, ws)
         if ev is not None:
             ev[2].record(stream)
-        if gather:
+        if slots:
+            G.grouped_ffn_slots(desc, h, b.src_token, b.src_slot, b.offsets, w1, w2, y_slots, ws)
+        elif gather:
             G.grouped_ffn_gather(desc, h, b.src_token, b.offsets, w1, w2, b.y_perm, ws)
         else:
             G.grouped_ffn(desc, b.x_perm, b.offsets, w1, w2, b.y_perm, ws)
         if ev is not None:
             ev[3].record(stream)
-        G.unpermute_combine(desc, b.y_perm, b.topk_idx, b.topk_gate, b.dest, y)
+        if slots:
+            G.combine_slots(desc, y_slots, b.topk_idx, b.topk_gate, b.dest, y)
+        else:
+            G.unpermute_combine(desc, b.y_perm, b.topk_idx, b.topk_gate, b.dest, y)
         if ev is not None:
             ev[4].record(stream)
 
@@ -442,8 +455,10 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.description}", "T": cfg.T, "d": cfg.d,
                    "E": cfg.E, "k": cfg.k, "d_ff": cfg.d_ff, "act": cfg.act, "gate": cfg.gate,
                    "experts_local": el, "capacity": capacity, "parallelism": "1 GPU",
-                   "dispatch": "rows gathered by the first expert GEMM" if gather
-                   else "rows copied into expert order"},
+                   "dispatch": ("rows gathered by the first expert GEMM, output written in "
+                                "(token, slot) order" if slots else
+                                "rows gathered by the first expert GEMM" if gather
+                                else "rows copied into expert order")},
         "roofline": {"kernel": "grouped expert FFN (tile map + SwiGLU GEMM + down GEMM)",
                      "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,

@@ -30,7 +30,8 @@ FLAG_ROW_OVERFLOW, FLAG_BAD_EXPERT_ID, FLAG_NONFINITE_LOGIT, FLAG_DROPPED = 1, 2
 
 EXPORTED = ("moe_capacity_from_factor", "moe_workspace_size", "moe_route",
             "moe_topk_from_logits", "moe_permute", "moe_grouped_ffn",
-            "moe_grouped_ffn_gather", "moe_pack_dedup", "moe_unpermute_combine",
+            "moe_grouped_ffn_gather", "moe_grouped_ffn_slots", "moe_pack_dedup",
+            "moe_unpermute_combine", "moe_combine_slots",
             "moe_layer_forward", "moe_status_str")
 
 
@@ -71,6 +72,8 @@ def _load():
         "moe_grouped_ffn": (I32, [D, P, P, P, P, P, P, SZ, P]),
         "moe_grouped_ffn_gather": (I32, [D, P, P, P, P, P, P, P, SZ, P]),
         "moe_pack_dedup": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "moe_grouped_ffn_slots": (I32, [D, P, P, P, P, P, P, P, P, SZ, P]),
+        "moe_combine_slots": (I32, [D, P, P, P, P, P, P]),
         "moe_unpermute_combine": (I32, [D, P, P, P, P, P, P]),
         "moe_layer_forward": (I32, [D, P, P, P, P, P, P, ctypes.POINTER(LayerBuffers), P, SZ, P]),
         "moe_status_str": (ctypes.c_char_p, [I32]),
@@ -275,6 +278,22 @@ def grouped_ffn_gather(desc, h, src_token, offsets, w1, w2, y_perm, ws, stream=N
         wsp, wsn, _stream(stream)), "moe_grouped_ffn_gather")
 
 
+def grouped_ffn_slots(desc, h, src_token, src_slot, offsets, w1, w2, y_slots, ws, stream=None):
+    """Gathered first GEMM; the second writes each grouped row to its
+    (token, slot) row of y_slots [T*k, d]."""
+    dt = torch_dtype(desc)
+    s1, s2 = _w_shapes(desc)
+    T, R, d, k = desc.T, desc.max_rows, desc.d, desc.k
+    wsp, wsn = _ws(ws)
+    _check(_lib.moe_grouped_ffn_slots(
+        ctypes.byref(desc), _ptr(h, "h", dt, (T, d)),
+        _ptr(src_token, "src_token", torch.int32, (R,)),
+        _ptr(src_slot, "src_slot", torch.int32, (R,)),
+        _ptr(offsets, "offsets", torch.int32, (desc.E + 1,)),
+        _ptr(w1, "w1", dt, s1), _ptr(w2, "w2", dt, s2), _ptr(y_slots, "y_slots", dt, (T * k, d)),
+        wsp, wsn, _stream(stream)), "moe_grouped_ffn_slots")
+
+
 def max_pairs(desc) -> int:
     """Rows of a deduplicated send buffer: T * min(k, ep_size)."""
     return desc.T * min(desc.k, desc.ep_size)
@@ -309,6 +328,17 @@ def unpermute_combine(desc, y_perm, topk_idx, topk_gate, dest, y, stream=None):
         _ptr(topk_gate, "topk_gate", torch.float32, (T, k)),
         _ptr(dest, "dest", torch.int32, (T, k)), _ptr(y, "y", dt, (T, d)),
         _stream(stream)), "moe_unpermute_combine")
+
+
+def combine_slots(desc, y_slots, topk_idx, topk_gate, dest, y, stream=None):
+    dt = torch_dtype(desc)
+    T, d, k = desc.T, desc.d, desc.k
+    _check(_lib.moe_combine_slots(
+        ctypes.byref(desc), _ptr(y_slots, "y_slots", dt, (T * k, d)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
+        _ptr(topk_gate, "topk_gate", torch.float32, (T, k)),
+        _ptr(dest, "dest", torch.int32, (T, k)), _ptr(y, "y", dt, (T, d)),
+        _stream(stream)), "moe_combine_slots")
 
 
 def layer_forward(desc, h, w_router, bias, w1, w2, y, bufs: LayerBuffersT, ws, stream=None):

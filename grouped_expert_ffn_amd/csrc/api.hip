@@ -153,13 +153,15 @@ static moe_status_t do_permute(const moe_layer_desc_t& d, const void* h, const i
 
 // rows == null: x holds the expert-ordered rows (x_perm); otherwise x is h and
 // row i of the grouped operand is h[rows[i]]
+// o_tok != null: grouped row r is written to row o_tok[r] * k + o_slot[r]
 static moe_status_t do_ffn(const moe_layer_desc_t& d, const void* x, const int32_t* rows,
                            const int32_t* offsets, const void* w1, const void* w2, void* y_perm,
-                           char* ws, hipStream_t s) {
+                           char* ws, hipStream_t s, const int32_t* o_tok = nullptr,
+                           const int32_t* o_slot = nullptr) {
   const Workspace w = workspace_layout(d);
   if (d.max_rows == 0) return MOE_OK;
   HIP_TRY(launch_grouped_ffn(d, x, rows, offsets, w1, w2, y_perm, ws + w.act,
-                             reinterpret_cast<int4*>(ws + w.gemm_tiles), s));
+                             reinterpret_cast<int4*>(ws + w.gemm_tiles), s, o_tok, o_slot));
   return MOE_OK;
 }
 
@@ -172,10 +174,17 @@ static moe_status_t check_gather(const moe_layer_desc_t& d) {
 }
 
 static moe_status_t do_combine(const moe_layer_desc_t& d, const void* y_perm, const int32_t* idx,
-                               const float* gate, const int32_t* dest, void* y, hipStream_t s) {
+                               const float* gate, const int32_t* dest, void* y, hipStream_t s,
+                               bool slots = false) {
   const int el = d.E / d.ep_size;
   HIP_TRY(launch_combine(y_perm, idx, gate, dest, y, d.T, d.k, d.d, d.dtype, d.ep_rank * el,
-                         (d.ep_rank + 1) * el, s));
+                         (d.ep_rank + 1) * el, s, slots));
+  return MOE_OK;
+}
+
+// slot rows [T*k, d] are indexed with 32-bit row numbers
+static moe_status_t check_slots(const moe_layer_desc_t& d) {
+  if (d.T * (int64_t)d.k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -271,6 +280,37 @@ MOE_EXPORT moe_status_t moe_grouped_ffn_gather(const moe_layer_desc_t* desc, con
                             {offsets, d.E + 1, false}}));
   MOE_TRY(check_ws(desc, ws, ws_bytes));
   return do_ffn(d, h, src_token, offsets, w1, w2, y_perm, (char*)ws, (hipStream_t)stream);
+}
+
+MOE_EXPORT moe_status_t moe_grouped_ffn_slots(const moe_layer_desc_t* desc, const void* h,
+                                              const int32_t* src_token, const int32_t* src_slot,
+                                              const int32_t* offsets, const void* w1,
+                                              const void* w2, void* y_slots, void* ws,
+                                              size_t ws_bytes, void* stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_layer_desc_t& d = *desc;
+  MOE_TRY(check_gather(d));
+  MOE_TRY(check_slots(d));
+  const int64_t R = d.max_rows, el = d.E / d.ep_size;
+  const int64_t w1n = el * (d.act == MOE_ACT_SWIGLU ? 2 : 1) * d.d_ff * d.d, w2n = el * d.d * d.d_ff;
+  MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {src_token, R, false}, {src_slot, R, false},
+                            {y_slots, d.T * d.k * d.d, true}, {w1, w1n, true}, {w2, w2n, true},
+                            {offsets, d.E + 1, false}}));
+  MOE_TRY(check_ws(desc, ws, ws_bytes));
+  return do_ffn(d, h, src_token, offsets, w1, w2, y_slots, (char*)ws, (hipStream_t)stream,
+                src_token, src_slot);
+}
+
+MOE_EXPORT moe_status_t moe_combine_slots(const moe_layer_desc_t* desc, const void* y_slots,
+                                          const int32_t* topk_idx, const float* topk_gate,
+                                          const int32_t* dest, void* y, void* stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_layer_desc_t& d = *desc;
+  MOE_TRY(check_slots(d));
+  const int64_t Tk = d.T * d.k;
+  MOE_TRY(check_bufs(desc, {{y_slots, Tk * d.d, true}, {topk_idx, Tk, false},
+                            {topk_gate, Tk, false}, {dest, Tk, false}, {y, d.T * d.d, true}}));
+  return do_combine(d, y_slots, topk_idx, topk_gate, dest, y, (hipStream_t)stream, true);
 }
 
 MOE_EXPORT moe_status_t moe_pack_dedup(const moe_layer_desc_t* desc, const void* h,

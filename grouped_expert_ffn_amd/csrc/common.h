@@ -71,13 +71,16 @@ hipError_t launch_pack_dedup(const void* h, const int32_t* idx, const int32_t* d
                              int32_t* recv_rows, const DedupScratch& w, int64_t T, int E, int k,
                              int ep_size, int ep_rank, int64_t max_rows, int row_bytes,
                              hipStream_t s);
+// slots: y_perm holds slot rows [T*k, d] (row t*k + j for slot j of token t)
+// instead of expert-ordered rows addressed through dest
 hipError_t launch_combine(const void* y_perm, const int32_t* idx, const float* gate,
                           const int32_t* dest, void* y, int64_t T, int k, int d, int dtype,
-                          int e_lo, int e_hi, hipStream_t s);
+                          int e_lo, int e_hi, hipStream_t s, bool slots = false);
 
 hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
                               const int32_t* rows, const int32_t* offsets, const void* w1,
                               const void* w2, void* y_perm, void* act, int4* tiles,
-                              hipStream_t s);
+                              hipStream_t s, const int32_t* o_tok = nullptr,
+                              const int32_t* o_slot = nullptr);
 
 }  // namespace moe

@@ -568,7 +568,7 @@ template <int U>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(
     const bf16x8* __restrict__ yp, const int32_t* __restrict__ idx,
     const float* __restrict__ gate, const int32_t* __restrict__ dest, bf16x8* __restrict__ y,
-    int64_t T, int k, int row_vec, int e_lo, int e_hi) {
+    int64_t T, int k, int row_vec, int e_lo, int e_hi, bool slots) {
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nw) {
@@ -578,7 +578,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
       int r = dest[t * k + lane];
       int e = idx[t * k + lane];
       if (r >= 0 && e >= e_lo && e < e_hi) {
-        mine = r;
+        mine = slots ? (int)(t * k + lane) : r;
         gm = gate[t * k + lane];
       }
     }
@@ -633,7 +633,7 @@ template <int KT, int U>
 __global__ __launch_bounds__(256) void combine_bf16_k_kernel(
     const bf16x8* __restrict__ yp, const int32_t* __restrict__ idx,
     const float* __restrict__ gate, const int32_t* __restrict__ dest, bf16x8* __restrict__ y,
-    int64_t T, int row_vec, int e_lo, int e_hi) {
+    int64_t T, int row_vec, int e_lo, int e_hi, bool slots) {
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nw) {
@@ -643,7 +643,7 @@ __global__ __launch_bounds__(256) void combine_bf16_k_kernel(
       int r = dest[t * KT + lane];
       int e = idx[t * KT + lane];
       if (r >= 0 && e >= e_lo && e < e_hi) {
-        mine = r;
+        mine = slots ? (int)(t * KT + lane) : r;
         gm = gate[t * KT + lane];
       }
     }
@@ -696,7 +696,7 @@ __global__ __launch_bounds__(256) void combine_bf16_k_kernel(
 __global__ __launch_bounds__(256) void combine_f32_kernel(
     const float* __restrict__ yp, const int32_t* __restrict__ idx,
     const float* __restrict__ gate, const int32_t* __restrict__ dest, float* __restrict__ y,
-    int64_t T, int k, int d, int e_lo, int e_hi) {
+    int64_t T, int k, int d, int e_lo, int e_hi, bool slots) {
   const int lane = threadIdx.x & 63;
   const int64_t nw = (int64_t)gridDim.x * 4;
   for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nw) {
@@ -705,7 +705,8 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(
       for (int j = 0; j < k; ++j) {
         int r = dest[t * k + j];
         int e = idx[t * k + j];
-        if (r >= 0 && e >= e_lo && e < e_hi) acc = fmaf(gate[t * k + j], yp[(int64_t)r * d + c], acc);
+        const int64_t row = slots ? t * k + j : r;
+        if (r >= 0 && e >= e_lo && e < e_hi) acc = fmaf(gate[t * k + j], yp[row * d + c], acc);
       }
       y[t * d + c] = acc;
     }
@@ -714,7 +715,7 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(
 
 hipError_t launch_combine(const void* y_perm, const int32_t* idx, const float* gate,
                           const int32_t* dest, void* y, int64_t T, int k, int d, int dtype,
-                          int e_lo, int e_hi, hipStream_t s) {
+                          int e_lo, int e_hi, hipStream_t s, bool slots) {
   if (T == 0) return hipSuccess;
   int64_t blocks = min((T + 3) / 4, (int64_t)device_cu_count() * 16);
   if (dtype == MOE_DTYPE_BF16) {
@@ -723,16 +724,17 @@ hipError_t launch_combine(const void* y_perm, const int32_t* idx, const float* g
     const int rv = d / 8;
     const dim3 g((unsigned)blocks), b(256);
     switch (k) {
-      case 1: hipLaunchKernelGGL((combine_bf16_k_kernel<1, 4>), g, b, 0, s, yp, idx, gate, dest, yo, T, rv, e_lo, e_hi); break;
-      case 2: hipLaunchKernelGGL((combine_bf16_k_kernel<2, 4>), g, b, 0, s, yp, idx, gate, dest, yo, T, rv, e_lo, e_hi); break;
-      case 4: hipLaunchKernelGGL((combine_bf16_k_kernel<4, 2>), g, b, 0, s, yp, idx, gate, dest, yo, T, rv, e_lo, e_hi); break;
+      case 1: hipLaunchKernelGGL((combine_bf16_k_kernel<1, 4>), g, b, 0, s, yp, idx, gate, dest, yo, T, rv, e_lo, e_hi, slots); break;
+      case 2: hipLaunchKernelGGL((combine_bf16_k_kernel<2, 4>), g, b, 0, s, yp, idx, gate, dest, yo, T, rv, e_lo, e_hi, slots); break;
+      case 4: hipLaunchKernelGGL((combine_bf16_k_kernel<4, 2>), g, b, 0, s, yp, idx, gate, dest, yo, T, rv, e_lo, e_hi, slots); break;
       default:
         hipLaunchKernelGGL(combine_bf16_kernel<4>, g, b, 0, s, yp, idx, gate, dest, yo, T, k, rv,
-                           e_lo, e_hi);
+                           e_lo, e_hi, slots);
     }
   } else {
     hipLaunchKernelGGL(combine_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       (const float*)y_perm, idx, gate, dest, (float*)y, T, k, d, e_lo, e_hi);
+                       (const float*)y_perm, idx, gate, dest, (float*)y, T, k, d, e_lo, e_hi,
+                       slots);
   }
   return hipGetLastError();
 }

@@ -75,7 +75,8 @@ template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, 
 __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ rows, const bf16* __restrict__ W,
     bf16* __restrict__ C, const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr,
-    int N, int K, int64_t w_stride, int n_n, int64_t ldc) {
+    int N, int K, int64_t w_stride, int n_n, int64_t ldc, const int32_t* __restrict__ o_tok,
+    const int32_t* __restrict__ o_slot, int o_k) {
   using TG = TileGemmDL<BM, BN, WM, WN, EPI, BK, MF, GA>;
   __shared__ __attribute__((aligned(1024))) bf16 lds[TG::LDS_ELEMS];
   const int n_m = *n_mt_ptr;
@@ -97,6 +98,9 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
     t.b = W + (int64_t)ex * w_stride + (int64_t)t.n0 * K;
     t.c_row = ey;
     t.nk = nk;
+    t.o_tok = o_tok;
+    t.o_slot = o_slot;
+    t.o_k = o_k;
     return true;
   };
   TG::run_tiles(get, N, K, C, ldc, lds);
@@ -116,7 +120,8 @@ struct TailPieces {
                                        TileGemmDL<HM, HN, WM, WN, EPI, BK, MF, GA, 2>>::type;
   __device__ static void run(const bf16* A, const int32_t* rows, const bf16* W, bf16* C,
                              const int4* tiles, int n_m, int first, int left, int N, int K,
-                             int64_t w_stride, int n_n, int64_t ldc, bf16* lds) {
+                             int64_t w_stride, int n_n, int64_t ldc, const int32_t* o_tok,
+                             const int32_t* o_slot, int o_k, bf16* lds) {
     const int units = S * left;
     const int nk = K / BK;
     const int slot = xcd_virtual_id(blockIdx.x, gridDim.x, 0);
@@ -139,6 +144,9 @@ struct TailPieces {
         t.b = W + (int64_t)ex * w_stride + (int64_t)n0 * K;
         t.c_row = ey;
         t.nk = nk;
+        t.o_tok = o_tok;
+        t.o_slot = o_slot;
+        t.o_k = o_k;
         return true;
       }
       return false;
@@ -154,7 +162,8 @@ template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, 
 __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ rows, const bf16* __restrict__ W,
     bf16* __restrict__ C, const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr,
-    int N, int K, int64_t w_stride, int n_n, int64_t ldc, int G) {
+    int N, int K, int64_t w_stride, int n_n, int64_t ldc, const int32_t* __restrict__ o_tok,
+    const int32_t* __restrict__ o_slot, int o_k, int G) {
   using P2 = TailPieces<2, 1, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
   using P4 = TailPieces<2, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
   using P8 = TailPieces<4, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
@@ -167,30 +176,35 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
   const int left = total - first;
   if (left == 0) return;
   if (8 * left <= G)
-    P8::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, lds);
+    P8::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot, o_k,
+            lds);
   else if (4 * left <= G)
-    P4::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, lds);
+    P4::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot, o_k,
+            lds);
   else
-    P2::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, lds);
+    P2::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot, o_k,
+            lds);
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA = false>
 static hipError_t grouped_gemm_dl_launch(const bf16* A, const int32_t* rows, const bf16* W,
                                          bf16* C, const int4* tiles, const int* n_mt, int N,
                                          int K, int64_t w_stride, int64_t ldc,
-                                         int64_t max_mtiles, int per_cu, hipStream_t s) {
+                                         int64_t max_mtiles, int per_cu, hipStream_t s,
+                                         const int32_t* o_tok = nullptr,
+                                         const int32_t* o_slot = nullptr, int o_k = 0) {
   const int n_n = (N + BN - 1) / BN;
   const int64_t ub = max_mtiles * n_n;
   int64_t G = min(((ub + 7) / 8) * 8, (int64_t)device_cu_count() * per_cu);
   G = max((int64_t)8, G / 8 * 8);
   hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>),
                      dim3((unsigned)G), dim3(64 * WM * WN), 0, s, A, rows, W, C, tiles, n_mt, N,
-                     K, w_stride, n_n, ldc);
+                     K, w_stride, n_n, ldc, o_tok, o_slot, o_k);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((grouped_gemm_tail_kernel<BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>),
                      dim3((unsigned)G), dim3(64 * WM * WN), 0, s, A, rows, W, C, tiles, n_mt, N,
-                     K, w_stride, n_n, ldc, (int)G);
+                     K, w_stride, n_n, ldc, o_tok, o_slot, o_k, (int)G);
   return hipGetLastError();
 }
 
@@ -204,7 +218,8 @@ template <int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     const float* __restrict__ A, const int32_t* __restrict__ a_rows, const float* __restrict__ W,
     float* __restrict__ C, const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr,
-    int N, int K, int64_t w_stride, int64_t ldc) {
+    int N, int K, int64_t w_stride, int64_t ldc, const int32_t* __restrict__ o_tok,
+    const int32_t* __restrict__ o_slot, int o_k) {
   const int mt = blockIdx.x;
   if (mt >= *n_mt_ptr) return;
   const int4 t = tiles[mt];
@@ -242,13 +257,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
   for (int i = 0; i < 4; ++i) {
     int m = ty * 4 + i;
     if (m >= rows) continue;
+    // o_tok: output row of grouped row r is the row of its (token, slot) pair
+    const int64_t r = t.y + m;
+    const int64_t orow = o_tok ? (int64_t)o_tok[r] * o_k + o_slot[r] : r;
     for (int j = 0; j < 4; ++j) {
       int n = n0 + tx * 4 + j;
       if (n >= N) continue;
       float v = acc[i][j];
       if (EPI == 1) v = fmaxf(v, 0.f);
       if (EPI == 2) v = v / (1.0f + expf(-v)) * accu[i][j];
-      C[(int64_t)(t.y + m) * ldc + n] = v;
+      C[orow * ldc + n] = v;
     }
   }
 }
@@ -257,10 +275,12 @@ template <int EPI>
 static hipError_t grouped_gemm_f32_launch(const float* A, const int32_t* a_rows, const float* W,
                                           float* C, const int4* tiles, const int* n_mt, int N,
                                           int K, int64_t w_stride, int64_t ldc,
-                                          int64_t max_mtiles, hipStream_t s) {
+                                          int64_t max_mtiles, hipStream_t s,
+                                          const int32_t* o_tok = nullptr,
+                                          const int32_t* o_slot = nullptr, int o_k = 0) {
   dim3 grid((unsigned)max_mtiles, (unsigned)((N + 63) / 64));
   hipLaunchKernelGGL(grouped_gemm_f32_kernel<EPI>, grid, dim3(256), 0, s, A, a_rows, W, C, tiles,
-                     n_mt, N, K, w_stride, ldc);
+                     n_mt, N, K, w_stride, ldc, o_tok, o_slot, o_k);
   return hipGetLastError();
 }
 
@@ -280,11 +300,12 @@ int64_t gemm_max_mtiles(const moe_layer_desc_t& d) {
 }
 
 // x_perm: the expert-ordered rows, or (gathered, rows != null) the token rows
-// h, read through rows = src_token.
+// h, read through rows = src_token. o_tok == null: grouped row r of the output
+// goes to row r of y_perm; otherwise to row o_tok[r] * k + o_slot[r].
 hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
                               const int32_t* rows, const int32_t* offsets, const void* w1,
                               const void* w2, void* y_perm, void* act, int4* tiles,
-                              hipStream_t s) {
+                              hipStream_t s, const int32_t* o_tok, const int32_t* o_slot) {
   const int el = desc.E / desc.ep_size;
   const int e_lo = desc.ep_rank * el;
   const int64_t max_mt = gemm_max_mtiles(desc);
@@ -314,6 +335,10 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
       err = grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_RELU_BF16, 64, kGemmGroupM, 16>(
           X, nullptr, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s);
     if (err != hipSuccess) return err;
+    if (o_tok)
+      return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_SLOTS_BF16, 64, kGemmGroupM, 16>(
+          H, nullptr, (const bf16*)w2, (bf16*)y_perm, tiles, n_mt, d, dff, (int64_t)d * dff, d,
+          mt_ub, 1, s, o_tok, o_slot, desc.k);
     return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_STORE_BF16, 64, kGemmGroupM, 16>(
         H, nullptr, (const bf16*)w2, (bf16*)y_perm, tiles, n_mt, d, dff, (int64_t)d * dff, d,
         mt_ub, 1, s);
@@ -330,7 +355,7 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
                                      (int64_t)w1_rows * d, dff, max_mt, s);
   if (err != hipSuccess) return err;
   return grouped_gemm_f32_launch<0>(H, nullptr, (const float*)w2, (float*)y_perm, tiles, n_mt, d,
-                                    dff, (int64_t)d * dff, d, max_mt, s);
+                                    dff, (int64_t)d * dff, d, max_mt, s, o_tok, o_slot, desc.k);
 }
 
 }  // namespace moe

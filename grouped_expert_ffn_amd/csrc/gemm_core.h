@@ -20,7 +20,15 @@
 
 namespace moe {
 
-enum Epilogue { EPI_STORE_BF16 = 0, EPI_SWIGLU_BF16 = 1, EPI_ROUTER_F32 = 2, EPI_RELU_BF16 = 3 };
+// EPI_SLOTS_BF16 stores like EPI_STORE_BF16, but grouped row r goes to output
+// row o_tok[r] * o_k + o_slot[r] (the row of its (token, slot) pair)
+enum Epilogue {
+  EPI_STORE_BF16 = 0,
+  EPI_SWIGLU_BF16 = 1,
+  EPI_ROUTER_F32 = 2,
+  EPI_RELU_BF16 = 3,
+  EPI_SLOTS_BF16 = 4
+};
 
 // SiLU with the hardware reciprocal (about 1 ulp): g * 1 / (1 + e^-g)
 __device__ __forceinline__ float silu_f(float g) {
@@ -73,6 +81,9 @@ struct GemmTile {
   int nk;           // K slices (of BK) to multiply
   const int32_t* rows;   // gathered A rows only: the tile's A row i is row rows[i]
                          // of the matrix at `a` (then `a` is that matrix's base)
+  const int32_t* o_tok;  // EPI_SLOTS_BF16 only: token and slot of each grouped row
+  const int32_t* o_slot;
+  int o_k;
 };
 
 // Persistent tile loop of one workgroup: run_tiles(get, ...) multiplies the
@@ -330,6 +341,9 @@ struct TileGemmDL {
       for (int y = 0; y < TM; ++y) {
         const int m = wm * WTM + y * MF + lr;
         if (m >= t.a_rows) continue;
+        int64_t orow = t.c_row + m;
+        if constexpr (EPI == EPI_SLOTS_BF16)
+          orow = (int64_t)t.o_tok[orow] * t.o_k + t.o_slot[orow];
 #pragma unroll
         for (int x = 0; x < TN; ++x) {
 #pragma unroll
@@ -342,7 +356,7 @@ struct TileGemmDL {
                 if (n + i < n_store) out[n + i] = acc[x][y][4 * g + i] + (bias ? bias[n + i] : 0.0f);
             } else {
               if (n >= N) continue;
-              bf16* out = reinterpret_cast<bf16*>(Cv) + (t.c_row + m) * ldc;
+              bf16* out = reinterpret_cast<bf16*>(Cv) + orow * ldc;
               bf16x4 o;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {

@@ -168,7 +168,8 @@ moe_status_t moe_grouped_ffn(const moe_layer_desc_t* desc, const void* x_perm,
  * of an expert's group is read straight from h [T,d] at token src_token[r]
  * (the inverse map moe_permute writes), so the rows are never copied into
  * x_perm. h may also be a deduplicated send buffer from moe_pack_dedup,
- * with its recv_rows in place of src_token. "Dropless MoE Is a Runtime Problem as Much as a Model Design",
+ * with its recv_rows in place of src_token.
+ * "Dropless MoE Is a Runtime Problem as Much as a Model Design",
  * expert-parallelism paragraph: fusing dispatch into the expert computation
  * removes an intermediate write and its read. Results are bit-identical to
  * moe_grouped_ffn on x_perm. bf16 needs T*min(k,ep_size)*d*2 bytes below
@@ -177,6 +178,22 @@ moe_status_t moe_grouped_ffn_gather(const moe_layer_desc_t* desc, const void* h,
                                     const int32_t* src_token, const int32_t* offsets,
                                     const void* w1, const void* w2, void* y_perm, void* ws,
                                     size_t ws_bytes, void* stream);
+
+/* Both ends of the grouped expert FFN fused with the data movement around
+ * it: the first GEMM reads token rows from h through src_token (as
+ * moe_grouped_ffn_gather), and the second GEMM's epilogue writes grouped row
+ * r to row src_token[r] * k + src_slot[r] of y_slots [T*k, d], the row of its
+ * (token, slot) pair, so that moe_combine_slots reads each token's k rows
+ * contiguously. Same page and paragraph as moe_grouped_ffn_gather (fusing
+ * dispatch and combine into the expert computation). The rows written hold
+ * the same bits as y_perm[dest] of moe_grouped_ffn; rows of slots not
+ * computed here (dropped, remote or past max_rows) are left untouched.
+ * Needs T*k < 2^31 and the bf16 size limit of moe_grouped_ffn_gather
+ * (MOE_ERR_SHAPE otherwise). */
+moe_status_t moe_grouped_ffn_slots(const moe_layer_desc_t* desc, const void* h,
+                                   const int32_t* src_token, const int32_t* src_slot,
+                                   const int32_t* offsets, const void* w1, const void* w2,
+                                   void* y_slots, void* ws, size_t ws_bytes, void* stream);
 
 /* Expert-parallel packing with token deduplication: one send row per
  * (destination rank, token) pair instead of one per (token, slot).
@@ -210,6 +227,15 @@ moe_status_t moe_pack_dedup(const moe_layer_desc_t* desc, const void* h, const i
 moe_status_t moe_unpermute_combine(const moe_layer_desc_t* desc, const void* y_perm,
                                    const int32_t* topk_idx, const float* topk_gate,
                                    const int32_t* dest, void* y, void* stream);
+
+/* The same combine on slot rows: y[t] = sum_j topk_gate[t,j] *
+ * y_slots[t*k + j] over the slots moe_unpermute_combine would use (dest >= 0,
+ * expert local), in the same float32 order, so y is bit-identical to
+ * moe_unpermute_combine on y_perm. y_slots [T*k, d] as written by
+ * moe_grouped_ffn_slots; dest [T,k] from the plan. Needs T*k < 2^31. */
+moe_status_t moe_combine_slots(const moe_layer_desc_t* desc, const void* y_slots,
+                               const int32_t* topk_idx, const float* topk_gate,
+                               const int32_t* dest, void* y, void* stream);
 
 /* Buffers of the fused call; all are required device pointers with the
  * shapes given above, except x_perm, which may be NULL: then the fused call

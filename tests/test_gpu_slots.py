@@ -1,0 +1,85 @@
+"""GPU parity of the slot-ordered FFN output (moe_grouped_ffn_slots) and its
+combine (moe_combine_slots): every computed slot row must hold the bits of
+y_perm[dest] from the plain path, rows of other slots stay untouched, and
+the combined output must equal moe_unpermute_combine's bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from tests.gpu_util import host, lib, run_layer, say, upload_layer
+from workloads import CONFIGS, make_inputs, small_layer_config
+
+pytestmark = pytest.mark.gpu
+
+
+def _slots_path(G, desc, dv, b, ws):
+    dt = G.torch_dtype(desc)
+    y_slots = torch.full((desc.T * desc.k, desc.d), float("nan"), dtype=dt, device="cuda")
+    G.grouped_ffn_slots(desc, dv["h"], b.src_token, b.src_slot, b.offsets, dv["w1"], dv["w2"],
+                        y_slots, ws)
+    y2 = torch.full((desc.T, desc.d), float("nan"), dtype=dt, device="cuda")
+    G.combine_slots(desc, y_slots, b.topk_idx, b.topk_gate, b.dest, y2)
+    torch.cuda.synchronize()
+    return y_slots, y2
+
+
+def _check(desc, b, y, y_slots, y2, el):
+    dest = host(b.dest).astype(np.int64)
+    idx = host(b.topk_idx).astype(np.int64)
+    local = (idx // el) == desc.ep_rank
+    used = (dest >= 0) & local
+    t, j = np.nonzero(used)
+    slots = torch.from_numpy(t * desc.k + j).cuda()
+    rows = torch.from_numpy(dest[t, j]).cuda()
+    assert torch.equal(y_slots[slots], b.y_perm[rows]), "slot rows differ from y_perm[dest]"
+    t2, j2 = np.nonzero(~used)
+    if len(t2):
+        untouched = y_slots[torch.from_numpy(t2 * desc.k + j2).cuda()]
+        assert torch.isnan(untouched.float()).all(), "rows of unused slots were written"
+    assert torch.equal(y2, y), "combine from slots differs from the plain combine"
+    return int(used.sum())
+
+
+# (layer, tokens, ep_size, ep_rank)
+CASES = [("tiny_fp32", 64, 1, 0), ("small_bf16", 1024, 1, 0), ("small_bf16", 1024, 4, 1),
+         ("mixtral_bf16", 256, 1, 0), ("finegrained_bf16", 1024, 1, 0),
+         ("ep_share_bf16", 512, 8, 0)]
+
+
+@pytest.mark.parametrize("name,T,ep,rank", CASES)
+def test_slot_rows_and_combine_bit_identical(name, T, ep, rank):
+    G = lib()
+    base = CONFIGS[name]
+    cfg = small_layer_config(base, T, ep_size=ep, ep_rank=rank)
+    inp = make_inputs(cfg)
+    for cf in base.capacity_factors:
+        cap = O.capacity_from_factor(cf, cfg.T, cfg.k, cfg.E)
+        say(f"slots {name} T={T} ep={ep}/{rank} cf={cf}")
+        desc, dv = upload_layer(G, cfg, inp, capacity=cap)
+        y, b, ws = run_layer(G, desc, dv)
+        y_slots, y2 = _slots_path(G, desc, dv, b, ws)
+        n = _check(desc, b, y, y_slots, y2, cfg.E // cfg.ep_size)
+        say(f"  {n} slot rows checked")
+
+
+def test_slots_with_rows_clamped_to_max_rows():
+    G = lib()
+    cfg = small_layer_config(CONFIGS["small_bf16"], 600)
+    inp = make_inputs(cfg)
+    desc, dv = upload_layer(G, cfg, inp, max_rows=900)
+    y, b, ws = run_layer(G, desc, dv)
+    assert int(host(b.flags)[0]) & G.FLAG_ROW_OVERFLOW
+    y_slots, y2 = _slots_path(G, desc, dv, b, ws)
+    _check(desc, b, y, y_slots, y2, cfg.E)
+
+
+@pytest.mark.slow
+def test_slots_full_mixtral_layer():
+    G = lib()
+    cfg = CONFIGS["mixtral_bf16"]
+    inp = make_inputs(cfg)
+    desc, dv = upload_layer(G, cfg, inp)
+    y, b, ws = run_layer(G, desc, dv)
+    y_slots, y2 = _slots_path(G, desc, dv, b, ws)
+    _check(desc, b, y, y_slots, y2, cfg.E)
