@@ -5,9 +5,10 @@
 // Both operands are K-contiguous, the natural layout for the bf16 MFMAs:
 // every lane feeds 8 consecutive K values of one row of each operand. K
 // slices of A and B stream from global memory straight into LDS (buffer or
-// global loads with the LDS bit, 16 bytes per lane), double-buffered. Each LDS row holds 16-byte
-// chunks stored at chunk ^ (row-dependent key), so the 16 rows one fragment
-// read touches fall in distinct banks of the 256-byte-wide LDS.
+// global loads with the LDS bit, 16 bytes per lane) through two or three
+// slice buffers. Each LDS row holds 16-byte chunks stored at chunk ^
+// (row-dependent key), so the 16 rows one fragment read touches fall in
+// distinct banks of the 256-byte-wide LDS.
 //
 // The MFMA is issued as D = W . X^T (weights as the first operand), so each
 // lane ends up holding four consecutive output columns of one row: stores of
@@ -88,8 +89,8 @@ struct GemmTile {
 
 // Persistent tile loop of one workgroup: run_tiles(get, ...) multiplies the
 // tiles get(0), get(1), ... until get returns false. K slices stream through
-// two LDS buffers as one sequence that runs across tile boundaries: the next
-// tile's first slices are already in flight while the current tile's
+// NBUF LDS buffers as one sequence that runs across tile boundaries: the
+// next tile's first slices are already in flight while the current tile's
 // epilogue converts and stores its accumulators.
 template <int BM, int BN, int WM, int WN, int EPI, int BK = 64, int MF = 16, bool GA = false,
           int NBUF = 2>
