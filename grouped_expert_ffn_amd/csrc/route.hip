@@ -5,6 +5,7 @@
 // deterministic tie handling: ids are ordered by score descending, equal
 // scores go to the lower expert id, -0 equals +0 and a NaN ranks below every
 // number (NaN or +-Inf raise MOE_FLAG_NONFINITE_LOGIT).
+#include <atomic>
 #include <type_traits>
 
 #include "gemm_core.h"
@@ -132,19 +133,21 @@ __global__ __launch_bounds__(64 * WM * WN) void router_tile_kernel(
   TG::run_tiles(get, E_pad, d, logits, E, lds, bias, E);
 }
 
-static int g_num_cu[64];
+// CU count per device, looked up once (concurrent first calls may both look it
+// up and store the same value)
+static std::atomic<int> g_num_cu[64];
 
 static int num_cus() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!g_num_cu[dev]) {
-    int n = 0;
+  int n = g_num_cu[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    g_num_cu[dev] = n;
+    g_num_cu[dev].store(n, std::memory_order_relaxed);
   }
-  return g_num_cu[dev];
+  return n;
 }
 
 int device_cu_count() { return num_cus(); }

@@ -15,7 +15,8 @@
  * ---------------------------------------
  *  - Every pointer argument except `desc` and `ws_bytes`-style sizes is a
  *    DEVICE pointer owned by the caller; the library allocates nothing, keeps
- *    no state between calls and never frees caller memory.
+ *    no state between calls (beyond a per-device cache of the CU count,
+ *    safe to fill from several threads) and never frees caller memory.
  *  - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *    the default stream). No entry point synchronises, copies device->host or
  *    reads device data on the host, so every call can be captured in a graph.
