@@ -182,12 +182,6 @@ static moe_status_t do_combine(const moe_layer_desc_t& d, const void* y_perm, co
   return MOE_OK;
 }
 
-// slot rows [T*k, d] are indexed with 32-bit row numbers
-static moe_status_t check_slots(const moe_layer_desc_t& d) {
-  if (d.T * (int64_t)d.k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
-  return MOE_OK;
-}
-
 }  // namespace moe
 
 using namespace moe;
@@ -290,7 +284,6 @@ MOE_EXPORT moe_status_t moe_grouped_ffn_slots(const moe_layer_desc_t* desc, cons
   MOE_TRY(check_desc(desc));
   const moe_layer_desc_t& d = *desc;
   MOE_TRY(check_gather(d));
-  MOE_TRY(check_slots(d));
   const int64_t R = d.max_rows, el = d.E / d.ep_size;
   const int64_t w1n = el * (d.act == MOE_ACT_SWIGLU ? 2 : 1) * d.d_ff * d.d, w2n = el * d.d * d.d_ff;
   MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {src_token, R, false}, {src_slot, R, false},
@@ -306,7 +299,6 @@ MOE_EXPORT moe_status_t moe_combine_slots(const moe_layer_desc_t* desc, const vo
                                           const int32_t* dest, void* y, void* stream) {
   MOE_TRY(check_desc(desc));
   const moe_layer_desc_t& d = *desc;
-  MOE_TRY(check_slots(d));
   const int64_t Tk = d.T * d.k;
   MOE_TRY(check_bufs(desc, {{y_slots, Tk * d.d, true}, {topk_idx, Tk, false},
                             {topk_gate, Tk, false}, {dest, Tk, false}, {y, d.T * d.d, true}}));

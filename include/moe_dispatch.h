@@ -78,7 +78,7 @@ typedef enum { MOE_ACT_RELU = 0, MOE_ACT_SWIGLU = 1 } moe_act_t;
 #define MOE_FLAG_DROPPED 8u         /* capacity dropped at least one assignment (informational) */
 
 typedef struct moe_layer_desc {
-  int64_t T;        /* tokens, >= 0 */
+  int64_t T;        /* tokens, >= 0, with T * k < 2^31 */
   int32_t d;        /* hidden width (bf16: multiple of 64) */
   int32_t E;        /* experts, global count, 1..1024 */
   int32_t k;        /* experts per token, 1..min(E, 16) */
@@ -189,8 +189,8 @@ moe_status_t moe_grouped_ffn_gather(const moe_layer_desc_t* desc, const void* h,
  * dispatch and combine into the expert computation). The rows written hold
  * the same bits as y_perm[dest] of moe_grouped_ffn; rows of slots not
  * computed here (dropped, remote or past max_rows) are left untouched.
- * Needs T*k < 2^31 and the bf16 size limit of moe_grouped_ffn_gather
- * (MOE_ERR_SHAPE otherwise). */
+ * Needs the bf16 size limit of moe_grouped_ffn_gather (MOE_ERR_SHAPE
+ * otherwise). */
 moe_status_t moe_grouped_ffn_slots(const moe_layer_desc_t* desc, const void* h,
                                    const int32_t* src_token, const int32_t* src_slot,
                                    const int32_t* offsets, const void* w1, const void* w2,
@@ -233,7 +233,7 @@ moe_status_t moe_unpermute_combine(const moe_layer_desc_t* desc, const void* y_p
  * y_slots[t*k + j] over the slots moe_unpermute_combine would use (dest >= 0,
  * expert local), in the same float32 order, so y is bit-identical to
  * moe_unpermute_combine on y_perm. y_slots [T*k, d] as written by
- * moe_grouped_ffn_slots; dest [T,k] from the plan. Needs T*k < 2^31. */
+ * moe_grouped_ffn_slots; dest [T,k] from the plan. */
 moe_status_t moe_combine_slots(const moe_layer_desc_t* desc, const void* y_slots,
                                const int32_t* topk_idx, const float* topk_gate,
                                const int32_t* dest, void* y, void* stream);
