@@ -27,7 +27,7 @@ Workspace workspace_layout(const moe_layer_desc_t& d) {
   const int64_t n_tiles = (d.T + kTokTile - 1) / kTokTile;
   off += align256((size_t)n_tiles * d.E * 4);
   w.gemm_tiles = off;
-  off += align256((size_t)(gemm_max_mtiles(d) + 1) * sizeof(int4));
+  off += align256((size_t)(2 * gemm_max_mtiles(d) + 1) * sizeof(int4));
   w.act = off;
   off += align256((size_t)d.max_rows * d.d_ff * elt_bytes(d.dtype));
   w.dedup = off;

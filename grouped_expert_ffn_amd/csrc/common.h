@@ -25,7 +25,8 @@ constexpr int kMaxK = 16;
 struct Workspace {
   size_t wrt;        // router weight transposed to [E_pad, d] bf16 (bf16 route only)
   size_t tile_hist;  // [n_tiles, E] int32 per-tile expert counts, then their prefixes
-  size_t gemm_tiles; // [max_mtiles] int4 grouped-GEMM tile table + count
+  size_t gemm_tiles; // [2, max_mtiles] int4 tile tables of the two expert GEMMs,
+                     // then their common length
   size_t act;        // [max_rows, d_ff] dtype: SwiGLU/ReLU activations
   size_t dedup;      // deduplicated packing: pid, first_row [T,k]; pair_slot [pairs];
                      // counts [E], offsets [E+1], flags [1] (int32)

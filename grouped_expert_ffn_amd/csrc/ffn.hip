@@ -16,34 +16,73 @@ namespace moe {
 int device_cu_count();
 
 // ---------------------------------------------------------------------------
-// Tile table: for local expert i, rows [offsets[lo+i], offsets[lo+i+1])
-// clamped to max_rows, cut into BM-row tiles. Table length at the end.
+// Tile tables, one per expert GEMM: for local expert i, rows
+// [offsets[lo+i], offsets[lo+i+1]) clamped to max_rows, cut into BM-row
+// tiles, in expert order. Table length (the same for both) at the end.
+//
+// An expert's last tile is short when it holds at most BM / 2 rows; the
+// GEMMs run a short tile on the lower half of their waves. The tiles past
+// the last whole round of a persistent grid of G workgroups go to a second
+// launch (when they fill at most half a round), cut into pieces. For each
+// GEMM (n_n column tiles per M-tile, grid G; G = 0: no reordering) with
+// such leftover tiles, the last k short M-tiles move to the end of its
+// table, k = enough whole groups of group_m M-tiles (the GEMMs walk the
+// table group_m M-tiles per column) to hold every leftover tile. That
+// launch then gets cheap tiles, and so does the round before it when the
+// moved tiles reach into it. Short tiles elsewhere keep their place beside
+// their expert's full tiles (a layer without leftover tiles keeps the plain
+// expert order).
 __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets,
                                                         int e_lo, int E_loc, int64_t max_rows,
-                                                        int BM, int4* __restrict__ tiles,
-                                                        int* __restrict__ n_tiles_out) {
-  __shared__ int scan[1024];
+                                                        int BM, int4* __restrict__ tiles1,
+                                                        int4* __restrict__ tiles2,
+                                                        int* __restrict__ n_tiles_out, int n_n1,
+                                                        int G1, int n_n2, int G2, int group_m) {
+  __shared__ int scan_m[1024], scan_s[1024];
   const int tid = threadIdx.x;
-  int r0 = 0, r1 = 0, mt = 0;
+  int r0 = 0, r1 = 0, mt = 0, sh = 0;
   if (tid < E_loc) {
     r0 = (int)min((int64_t)offsets[e_lo + tid], max_rows);
     r1 = (int)min((int64_t)offsets[e_lo + tid + 1], max_rows);
     mt = r1 > r0 ? (r1 - r0 + BM - 1) / BM : 0;
+    sh = (mt > 0 && r1 - r0 - (mt - 1) * BM <= BM / 2) ? 1 : 0;
   }
-  scan[tid] = mt;
+  scan_m[tid] = mt;
+  scan_s[tid] = sh;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
-    int add = tid >= o ? scan[tid - o] : 0;
+    const int am = tid >= o ? scan_m[tid - o] : 0;
+    const int as = tid >= o ? scan_s[tid - o] : 0;
     __syncthreads();
-    scan[tid] += add;
+    scan_m[tid] += am;
+    scan_s[tid] += as;
     __syncthreads();
   }
-  const int start = scan[tid] - mt;
-  for (int m = 0; m < mt; ++m) {
-    int a = r0 + m * BM;
-    tiles[start + m] = make_int4(tid, a, min(a + BM, r1), 0);
+  const int M = scan_m[1023], S = scan_s[1023];
+  for (int g = 0; g < 2; ++g) {
+    const int n_n = g ? n_n2 : n_n1, G = g ? G2 : G1;
+    int4* tab = g ? tiles2 : tiles1;
+    int k = 0;
+    if (G > 0 && M > 0) {
+      const int left = (int)((int64_t)M * n_n % G);
+      if (left > 0 && 2 * left <= G) {
+        const int last = M - (M - 1) / group_m * group_m;   // M-tiles in the last group
+        const int more = max(0, left - last * n_n);        // leftover tiles before it
+        k = min(S, last + (more + group_m * n_n - 1) / (group_m * n_n) * group_m);
+      }
+    }
+    // short M-tiles j = 0..S-1 in expert order; those with j >= S - k move
+    const int j = scan_s[tid] - sh;   // short M-tiles of the experts before this one
+    const int mv = (sh && j >= S - k) ? 1 : 0;
+    const int moved_before = max(0, j - (S - k));
+    const int start = scan_m[tid] - mt - moved_before;
+    for (int m = 0; m < mt - mv; ++m) {
+      const int a = r0 + m * BM;
+      tab[start + m] = make_int4(tid, a, min(a + BM, r1), 0);
+    }
+    if (mv) tab[M - k + j - (S - k)] = make_int4(tid, r0 + (mt - 1) * BM, r1, 0);
   }
-  if (tid == 1023) *n_tiles_out = scan[1023];
+  if (tid == 1023) *n_tiles_out = M;
 }
 
 // ---------------------------------------------------------------------------
@@ -186,6 +225,14 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
             lds);
 }
 
+// Persistent grid of the bf16 expert GEMMs: per_cu workgroups per CU, at
+// most the tile count's upper bound, a multiple of 8 (one share per XCD).
+static int gemm_grid(int64_t max_mtiles, int n_n, int per_cu) {
+  const int64_t ub = max_mtiles * n_n;
+  const int64_t G = min(((ub + 7) / 8) * 8, (int64_t)device_cu_count() * per_cu);
+  return (int)max((int64_t)8, G / 8 * 8);
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA = false>
 static hipError_t grouped_gemm_dl_launch(const bf16* A, const int32_t* rows, const bf16* W,
                                          bf16* C, const int4* tiles, const int* n_mt, int N,
@@ -194,9 +241,7 @@ static hipError_t grouped_gemm_dl_launch(const bf16* A, const int32_t* rows, con
                                          const int32_t* o_tok = nullptr,
                                          const int32_t* o_slot = nullptr, int o_k = 0) {
   const int n_n = (N + BN - 1) / BN;
-  const int64_t ub = max_mtiles * n_n;
-  int64_t G = min(((ub + 7) / 8) * 8, (int64_t)device_cu_count() * per_cu);
-  G = max((int64_t)8, G / 8 * 8);
+  const int G = gemm_grid(max_mtiles, n_n, per_cu);
   hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>),
                      dim3((unsigned)G), dim3(64 * WM * WN), 0, s, A, rows, W, C, tiles, n_mt, N,
                      K, w_stride, n_n, ldc, o_tok, o_slot, o_k);
@@ -309,15 +354,19 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
   const int el = desc.E / desc.ep_size;
   const int e_lo = desc.ep_rank * el;
   const int64_t max_mt = gemm_max_mtiles(desc);
-  int* n_mt = reinterpret_cast<int*>(tiles + max_mt);
+  int4* tiles2 = tiles + max_mt;   // the down GEMM's tile table
+  int* n_mt = reinterpret_cast<int*>(tiles + 2 * max_mt);
   const int d = desc.d, dff = desc.d_ff;
   const bool swiglu = desc.act == MOE_ACT_SWIGLU;
   const int w1_rows = swiglu ? 2 * dff : dff;
   hipError_t err;
   if (desc.dtype == MOE_DTYPE_BF16) {
-    hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,
-                       desc.max_rows, kGemmBM, tiles, n_mt);
     const int64_t mt_ub = (desc.max_rows + kGemmBM - 1) / kGemmBM + el;
+    const int n_n1 = (dff + (swiglu ? 127 : 255)) / (swiglu ? 128 : 256);   // GEMM1 BN
+    const int n_n2 = (d + 255) / 256;
+    hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,
+                       desc.max_rows, kGemmBM, tiles, tiles2, n_mt, n_n1,
+                       gemm_grid(mt_ub, n_n1, 1), n_n2, gemm_grid(mt_ub, n_n2, 1), kGemmGroupM);
     const bf16* X = (const bf16*)x_perm;
     const bf16* W1 = (const bf16*)w1;
     bf16* H = (bf16*)act;
@@ -337,14 +386,14 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
     if (err != hipSuccess) return err;
     if (o_tok)
       return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_SLOTS_BF16, 64, kGemmGroupM, 16>(
-          H, nullptr, (const bf16*)w2, (bf16*)y_perm, tiles, n_mt, d, dff, (int64_t)d * dff, d,
+          H, nullptr, (const bf16*)w2, (bf16*)y_perm, tiles2, n_mt, d, dff, (int64_t)d * dff, d,
           mt_ub, 1, s, o_tok, o_slot, desc.k);
     return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_STORE_BF16, 64, kGemmGroupM, 16>(
-        H, nullptr, (const bf16*)w2, (bf16*)y_perm, tiles, n_mt, d, dff, (int64_t)d * dff, d,
+        H, nullptr, (const bf16*)w2, (bf16*)y_perm, tiles2, n_mt, d, dff, (int64_t)d * dff, d,
         mt_ub, 1, s);
   }
   hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,
-                     desc.max_rows, kF32BM, tiles, n_mt);
+                     desc.max_rows, kF32BM, tiles, tiles2, n_mt, 0, 0, 0, 0, 1);
   const float* X = (const float*)x_perm;
   float* H = (float*)act;
   if (swiglu)

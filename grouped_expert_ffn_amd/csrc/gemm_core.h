@@ -92,6 +92,11 @@ struct GemmTile {
 // NBUF LDS buffers as one sequence that runs across tile boundaries: the
 // next tile's first slices are already in flight while the current tile's
 // epilogue converts and stores its accumulators.
+//
+// A tile whose valid rows all fall in the lower half of the
+// wave grid (a_rows <= BM / 2 with two wave rows) leaves the upper waves
+// idle: they still fetch their share of each slice and meet every barrier,
+// but issue no MFMAs, so the lower waves have their SIMDs to themselves.
 template <int BM, int BN, int WM, int WN, int EPI, int BK = 64, int MF = 16, bool GA = false,
           int NBUF = 2>
 struct TileGemmDL {
@@ -407,12 +412,17 @@ struct TileGemmDL {
     // exact inside a loop body but waits for everything at a loop head that
     // outstanding reads reach through the back edge.
     for (int c_idx = 0;; ++c_idx) {
+      // upper wave row with no valid row of this tile (wave-uniform): it
+      // skips the fragment reads, MFMAs and epilogue below
+      const bool busy = !(WM == 2 && wm == 1 && ct.a_rows <= WTM);
       // the tile's first slice is in LDS buffer cb
-      zero_acc();
-      read_b(cb, 0, b0);
+      if (busy) {
+        zero_acc();
+        read_b(cb, 0, b0);
 #pragma unroll
-      for (int y = 0; y < TM; ++y) fy[y] = read_a(cb, 0, y);
-      step(Yes{}, b0, b1, cb, 1);
+        for (int y = 0; y < TM; ++y) fy[y] = read_a(cb, 0, y);
+        step(Yes{}, b0, b1, cb, 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // slice g fully read by this wave; slice g+1 landed from this wave (and
       // the previous tile's stores drained)
@@ -422,9 +432,11 @@ struct TileGemmDL {
       for (int ck = 0; ck < ct.nk - 1; ++ck) {
         const int nb = next_buf(cb);
         issue_next();                          // slice g+NBUF into the buffer g left
-        step(Yes{}, b1, b0, nb, 0);            // last sub-step of g, reads g+1
-        __builtin_amdgcn_sched_barrier(0);
-        step(Yes{}, b0, b1, nb, 1);            // sub-step 0 of g+1, reads its sub-step 1
+        if (busy) {
+          step(Yes{}, b1, b0, nb, 0);          // last sub-step of g, reads g+1
+          __builtin_amdgcn_sched_barrier(0);
+          step(Yes{}, b0, b1, nb, 1);          // sub-step 0 of g+1, reads its sub-step 1
+        }
         __builtin_amdgcn_sched_barrier(0);
         wait_slice();                          // slice g+2 landed from this wave ...
         lds_barrier();                         // ... and slice g+1 read by every wave
@@ -434,10 +446,10 @@ struct TileGemmDL {
       // the tile's last slice; its epilogue runs while the next tile's first
       // slices load, and that tile's first fragments are read after it
       issue_next();
-      step(No{}, b1, b0, 0, 0);
+      if (busy) step(No{}, b1, b0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       cb = next_buf(cb);
-      epilogue(ct);
+      if (busy) epilogue(ct);
       // the load cursor has already looked up the tile after this one
       if (c_idx + 1 >= tiles_end) break;
       get(c_idx + 1, ct);

@@ -75,6 +75,38 @@ def test_rows_clamped_to_max_rows():
     _ffn_case(G, [100, 200], 128, 128, "swiglu", "bf16", max_rows=200, seed=7)
 
 
+def test_short_tiles_and_leftover_launch_keep_the_bits():
+    """Ten experts of 7 row tiles each, 8 of them ending in a tile of at most
+    half its rows. With 4 column tiles per row tile (d_ff = 512) the first GEMM
+    has 280 tiles: one whole round of a 256-workgroup grid plus 24 leftover
+    tiles, which go to the second launch; the tile table puts 6 short row
+    tiles last for that (two groups of row tiles), and short tiles run on half
+    of the waves. Outputs must match the oracle, and each expert's rows must
+    carry the same bits as when that expert runs alone (another table)."""
+    G = lib()
+    sizes = [6 * 256 + r for r in (16, 100, 128, 129, 200, 16, 24, 64, 84, 4)]
+    _ffn_case(G, sizes, 256, 512, "swiglu", "bf16", seed=11)
+    rng = np.random.default_rng(11)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(offsets[-1])
+    d, dff, el = 256, 512, len(sizes)
+    x = dev(_rand(rng, (rows, d), 1.0, "bf16"), torch.bfloat16)
+    w1 = dev(_rand(rng, (el, 2 * dff, d), d ** -0.5, "bf16"), torch.bfloat16)
+    w2 = dev(_rand(rng, (el, d, dff), dff ** -0.5, "bf16"), torch.bfloat16)
+    desc = G.make_desc(rows, d, el, 1, dff, "bf16", "softmax", "swiglu", max_rows=rows)
+    y = torch.zeros((rows, d), dtype=torch.bfloat16, device="cuda")
+    G.grouped_ffn(desc, x, dev(offsets), w1, w2, y, G.alloc_workspace(desc))
+    for e in range(el):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        de = G.make_desc(hi - lo, d, 1, 1, dff, "bf16", "softmax", "swiglu", max_rows=hi - lo)
+        ye = torch.zeros((hi - lo, d), dtype=torch.bfloat16, device="cuda")
+        G.grouped_ffn(de, x[lo:hi].contiguous(), dev(np.array([0, hi - lo], np.int32)),
+                      w1[e:e + 1].contiguous(), w2[e:e + 1].contiguous(), ye,
+                      G.alloc_workspace(de))
+        torch.cuda.synchronize()
+        assert torch.equal(ye, y[lo:hi]), f"expert {e} differs when run alone"
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("E,k,ep", [(8, 2, (1, 0)), (128, 8, (1, 0)), (256, 8, (8, 3)), (4, 1, (2, 1))])
 def test_unpermute_combine(dtype, E, k, ep):
