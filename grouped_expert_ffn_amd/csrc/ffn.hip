@@ -147,16 +147,18 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
 
 // The leftover tiles of the kernel above (same tile table, same order),
 // each cut into S = SM * SN pieces of BM / SM rows by BN / SN columns: unit
-// u is piece u % S of tile main_tile_end + u / S. One piece per workgroup;
-// fewer MFMAs per K slice than a whole tile, so the piece loop keeps three
-// slice buffers when they fit in the 160 KiB of LDS.
+// u is piece u % S of tile main_tile_end + u / S. One piece per workgroup.
+// A piece has few MFMAs per K slice (fewer still on a short tile), so its
+// loop waits on memory latency rather than on the MFMAs: it keeps as many
+// slice buffers (up to five, four slices in flight) as fit in the 160 KiB of
+// LDS.
 template <int SM, int SN, int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF,
           bool GA>
 struct TailPieces {
   static constexpr int HM = BM / SM, HN = BN / SN, S = SM * SN;
-  using TG3 = TileGemmDL<HM, HN, WM, WN, EPI, BK, MF, GA, 3>;
-  using TG = typename std::conditional<TG3::LDS_ELEMS * 2 <= 160 * 1024, TG3,
-                                       TileGemmDL<HM, HN, WM, WN, EPI, BK, MF, GA, 2>>::type;
+  static constexpr int BUF_BYTES = TileGemmDL<HM, HN, WM, WN, EPI, BK, MF, GA, 2>::LDS_BUF * 2;
+  static constexpr int NB = 160 * 1024 / BUF_BYTES;
+  using TG = TileGemmDL<HM, HN, WM, WN, EPI, BK, MF, GA, NB >= 5 ? 5 : NB < 2 ? 2 : NB>;
   __device__ static void run(const bf16* A, const int32_t* rows, const bf16* W, bf16* C,
                              const int4* tiles, int n_m, int first, int left, int N, int K,
                              int64_t w_stride, int n_n, int64_t ldc, const int32_t* o_tok,

@@ -119,7 +119,8 @@ struct TileGemmDL {
   static constexpr int NSUB = BK / KSUB;           // sub-steps per slice
   static constexpr int TU = GATED ? TN : 1;
   static_assert(MF == 16 || MF == 32, "MFMA shape");
-  static_assert(NBUF == 2 || NBUF == 3, "two or three slice buffers");
+  static_assert(NBUF >= 2 && NBUF <= 5, "two to five slice buffers");
+  static_assert((NBUF - 2) * LPW < 64, "slices in flight must fit the vmcnt field");
   static_assert(LOADS % NW == 0, "loads must split evenly over waves");
   static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be a multiple of the MFMA tile");
   static_assert(BK % 32 == 0 && NSUB >= 2, "two or more MFMA sub-steps per K slice");
@@ -232,13 +233,13 @@ struct TileGemmDL {
     if (!l_live) return;
     GemmTile ct = lt;   // tile being multiplied
     set_offsets(lt);
-    // the buffer the next slice goes to; whether the latest call issued loads
-    int l_buf = 0;
-    bool l_issued = false;
+    // the buffer the next slice goes to; slices issued so far (the slices of
+    // all tiles form one sequence)
+    int l_buf = 0, l_issued = 0;
     auto issue_next = [&]() {
-      l_issued = l_live;
       if (!l_live) return;
       issue(lt, l_k, l_buf);
+      ++l_issued;
       l_buf = l_buf + 1 == NBUF ? 0 : l_buf + 1;
       if (++l_k == lt.nk) {
         l_k = 0;
@@ -383,30 +384,37 @@ struct TileGemmDL {
     // barrier: sub-step 1 is read while sub-step 0 is multiplied, and sub-step
     // 0 of slice g+1 is read right after the barrier that publishes it, while
     // sub-step 1 of slice g is multiplied. Slice g+NBUF is fetched into the
-    // buffer slice g just left, so it has NBUF-1 slices of MFMAs to arrive.
+    // buffer slice g just left, so it has NBUF-1 slices of MFMAs to arrive
+    // (NBUF-2 whole slices, and the sub-steps around the barriers).
     // sched_barrier fences keep the compiler from moving MFMAs across the
     // slice barrier, which would leave the reads before it uncovered.
     static_assert(NSUB == 2, "the loop below pipelines two sub-steps per slice");
     using Yes = std::integral_constant<bool, true>;
     using No = std::integral_constant<bool, false>;
-    // Wait until the slice that the next barrier publishes has landed: with
-    // three buffers the latest slice's loads may stay in flight. Only loads
-    // are outstanding at these waits (the epilogue's stores are drained at
-    // the first barrier of the next tile), and loads complete in order.
-    auto wait_slice = [&]() {
-      if (NBUF == 3 && l_issued)
-        wait_vmcnt<LPW>();
+    // Wait until slice t, which the next barrier publishes, has landed from
+    // this wave: the slices issued after it (at most NBUF - 2) may stay in
+    // flight. Only loads are outstanding at these waits (the epilogue's
+    // stores are drained at the first barrier of the next tile), and loads
+    // complete in order.
+    auto wait_slice = [&](int t) {
+      const int n = l_issued - 1 - t;
+      if (NBUF >= 5 && n >= 3)
+        wait_vmcnt<(NBUF >= 5 ? 3 * LPW : 0)>();
+      else if (NBUF >= 4 && n >= 2)
+        wait_vmcnt<(NBUF >= 4 ? 2 * LPW : 0)>();
+      else if (NBUF >= 3 && n >= 1)
+        wait_vmcnt<(NBUF >= 3 ? LPW : 0)>();
       else
         wait_vmcnt<0>();
     };
     auto next_buf = [](int b) { return b + 1 == NBUF ? 0 : b + 1; };
-    issue_next();
-    if (NBUF == 3) issue_next();
-    wait_slice();
+    for (int i = 0; i < NBUF - 1; ++i) issue_next();
+    wait_slice(0);
     lds_barrier();
     issue_next();
     FragsB b0, b1;
     int cb = 0;   // LDS buffer of the slice being multiplied
+    int gc = 0;   // its index in the slice sequence
     // The slice loop is rotated so that its head follows a slice barrier,
     // where no LDS read is outstanding: the compiler's wait insertion is
     // exact inside a loop body but waits for everything at a loop head that
@@ -438,10 +446,11 @@ struct TileGemmDL {
           step(Yes{}, b0, b1, nb, 1);          // sub-step 0 of g+1, reads its sub-step 1
         }
         __builtin_amdgcn_sched_barrier(0);
-        wait_slice();                          // slice g+2 landed from this wave ...
+        wait_slice(gc + 2);                    // slice g+2 landed from this wave ...
         lds_barrier();                         // ... and slice g+1 read by every wave
         __builtin_amdgcn_sched_barrier(0);
         cb = nb;
+        ++gc;
       }
       // the tile's last slice; its epilogue runs while the next tile's first
       // slices load, and that tile's first fragments are read after it
@@ -449,6 +458,7 @@ struct TileGemmDL {
       if (busy) step(No{}, b1, b0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       cb = next_buf(cb);
+      ++gc;
       if (busy) epilogue(ct);
       // the load cursor has already looked up the tile after this one
       if (c_idx + 1 >= tiles_end) break;
