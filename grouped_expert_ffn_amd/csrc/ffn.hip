@@ -335,7 +335,8 @@ static hipError_t grouped_gemm_f32_launch(const float* A, const int32_t* a_rows,
 // bf16 expert GEMMs: 256-row M tiles, 8 waves (2 x 4), each wave a 128 x 64
 // block of 16x16x32 MFMAs; K slices of 64 stream into LDS by direct loads.
 // GEMM1 (SwiGLU) stages 128 gate + 128 up weight rows per tile and writes
-// 128 activation columns; GEMM2 stages 256 weight rows. Tiles are walked
+// 128 activation columns; GEMM2 stages 256 weight rows (128 for small layers,
+// where wave tiles are 128 x 32). Tiles are walked
 // 4 M-tiles per N column (GROUP_M = 4) in XCD-major order.
 constexpr int kGemmBM = 256;
 constexpr int kGemmGroupM = 4;
@@ -365,7 +366,12 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
   if (desc.dtype == MOE_DTYPE_BF16) {
     const int64_t mt_ub = (desc.max_rows + kGemmBM - 1) / kGemmBM + el;
     const int n_n1 = (dff + (swiglu ? 127 : 255)) / (swiglu ? 128 : 256);   // GEMM1 BN
-    const int n_n2 = (d + 255) / 256;
+    // down GEMM column tiles: 256 wide, or 128 wide when even the most tiles
+    // the layer can have (from max_rows, not from the routing) would leave
+    // part of one round of the grid idle; the K order of every output is the
+    // same either way
+    const bool narrow2 = mt_ub * ((d + 255) / 256) < device_cu_count();
+    const int n_n2 = narrow2 ? (d + 127) / 128 : (d + 255) / 256;
     hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,
                        desc.max_rows, kGemmBM, tiles, tiles2, n_mt, n_n1,
                        gemm_grid(mt_ub, n_n1, 1), n_n2, gemm_grid(mt_ub, n_n2, 1), kGemmGroupM);
@@ -386,13 +392,20 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
       err = grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_RELU_BF16, 64, kGemmGroupM, 16>(
           X, nullptr, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s);
     if (err != hipSuccess) return err;
+    const bf16* W2 = (const bf16*)w2;
+    bf16* Y = (bf16*)y_perm;
+    const int64_t s2 = (int64_t)d * dff;
+    if (o_tok && narrow2)
+      return grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_SLOTS_BF16, 64, kGemmGroupM, 16>(
+          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, o_tok, o_slot, desc.k);
     if (o_tok)
       return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_SLOTS_BF16, 64, kGemmGroupM, 16>(
-          H, nullptr, (const bf16*)w2, (bf16*)y_perm, tiles2, n_mt, d, dff, (int64_t)d * dff, d,
-          mt_ub, 1, s, o_tok, o_slot, desc.k);
+          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, o_tok, o_slot, desc.k);
+    if (narrow2)
+      return grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_STORE_BF16, 64, kGemmGroupM, 16>(
+          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s);
     return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_STORE_BF16, 64, kGemmGroupM, 16>(
-        H, nullptr, (const bf16*)w2, (bf16*)y_perm, tiles2, n_mt, d, dff, (int64_t)d * dff, d,
-        mt_ub, 1, s);
+        H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s);
   }
   hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,
                      desc.max_rows, kF32BM, tiles, tiles2, n_mt, 0, 0, 0, 0, 1);

@@ -4,9 +4,9 @@
 //
 // Both operands are K-contiguous, the natural layout for the bf16 MFMAs:
 // every lane feeds 8 consecutive K values of one row of each operand. K
-// slices of A and B stream from global memory straight into LDS (buffer or
-// global loads with the LDS bit, 16 bytes per lane) through two or three
-// slice buffers. Each LDS row holds 16-byte chunks stored at chunk ^
+// slices of A and B stream from global memory straight into LDS (buffer
+// loads with the LDS bit, 16 bytes per lane) through two to five slice
+// buffers. Each LDS row holds 16-byte chunks stored at chunk ^
 // (row-dependent key), so the 16 rows one fragment read touches fall in
 // distinct banks of the 256-byte-wide LDS.
 //
@@ -196,10 +196,11 @@ struct TileGemmDL {
     // is outstanding; with buffer loads its LDS-read waits stay exact.
     // Resource word 3 = 0x00020000 (32-bit data format, the raw-buffer setting
     // of this GPU family); the record count is the maximum, so no clamping.
+    // A wave whose loads straddle the A and weight rows keeps a resource for
+    // each and picks one per load (a scalar select; which rows a load fills
+    // depends only on the wave and the load's index).
     constexpr bool WAVE_UNIFORM = BM % (LPW * L::RPL) == 0;
     const bool wave_a = wave * LPW * L::RPL < BM;
-    // otherwise: a scalar base plus a 32-bit per-lane byte offset (the
-    // global load's saddr form), one VGPR per load
     auto issue = [&](const GemmTile& t, int kt, int buf) {
       bf16* base = lds + buf * LDS_BUF + wave * LPW * L::RPL * BK;
       const uint32_t ko = (uint32_t)kt * (BK * 2);
@@ -217,13 +218,18 @@ struct TileGemmDL {
         }
         return;
       }
+      const __amdgpu_buffer_rsrc_t ra =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(t.a), (short)0, -1, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rb =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(t.b), (short)0, -1, 0x00020000);
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         uint32_t o = off[i];
         if (GA && is_a[i])
           o = o * (uint32_t)(K * 2) + (((wave * LPW + i) & 1) ? chunk_odd : chunk_even);
-        const char* src = reinterpret_cast<const char*>(is_a[i] ? t.a : t.b) + (o + ko);
-        __builtin_amdgcn_global_load_lds(src, base + i * L::RPL * BK, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            is_a[i] ? ra : rb, (__attribute__((address_space(3))) void*)(base + i * L::RPL * BK),
+            16, o, ko, 0, 0);
       }
     };
     // load cursor: the tile and slice fetched next
