@@ -18,7 +18,9 @@ int device_cu_count();
 // ---------------------------------------------------------------------------
 // Tile tables, one per expert GEMM: for local expert i, rows
 // [offsets[lo+i], offsets[lo+i+1]) clamped to max_rows, cut into BM-row
-// tiles, in expert order. Table length (the same for both) at the end.
+// tiles, in expert order. Table length (the same for both) at the end,
+// then one word per GEMM: the most rows any of its leftover tiles holds when
+// all of them are short tiles moved there (see below), else 0.
 //
 // An expert's last tile is short when it holds at most BM / 2 rows; the
 // GEMMs run a short tile on the lower half of their waves. The tiles past
@@ -39,7 +41,9 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
                                                         int* __restrict__ n_tiles_out, int n_n1,
                                                         int G1, int n_n2, int G2, int group_m) {
   __shared__ int scan_m[1024], scan_s[1024];
+  __shared__ int moved_rows[2];
   const int tid = threadIdx.x;
+  if (tid < 2) moved_rows[tid] = 0;
   int r0 = 0, r1 = 0, mt = 0, sh = 0;
   if (tid < E_loc) {
     r0 = (int)min((int64_t)offsets[e_lo + tid], max_rows);
@@ -62,13 +66,14 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
   for (int g = 0; g < 2; ++g) {
     const int n_n = g ? n_n2 : n_n1, G = g ? G2 : G1;
     int4* tab = g ? tiles2 : tiles1;
-    int k = 0;
+    int k = 0, need = 0;
     if (G > 0 && M > 0) {
       const int left = (int)((int64_t)M * n_n % G);
       if (left > 0 && 2 * left <= G) {
         const int last = M - (M - 1) / group_m * group_m;   // M-tiles in the last group
         const int more = max(0, left - last * n_n);        // leftover tiles before it
-        k = min(S, last + (more + group_m * n_n - 1) / (group_m * n_n) * group_m);
+        need = last + (more + group_m * n_n - 1) / (group_m * n_n) * group_m;
+        k = min(S, need);
       }
     }
     // short M-tiles j = 0..S-1 in expert order; those with j >= S - k move
@@ -80,7 +85,12 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
       const int a = r0 + m * BM;
       tab[start + m] = make_int4(tid, a, min(a + BM, r1), 0);
     }
-    if (mv) tab[M - k + j - (S - k)] = make_int4(tid, r0 + (mt - 1) * BM, r1, 0);
+    if (mv) {
+      tab[M - k + j - (S - k)] = make_int4(tid, r0 + (mt - 1) * BM, r1, 0);
+      atomicMax(&moved_rows[g], r1 - r0 - (mt - 1) * BM);
+    }
+    __syncthreads();
+    if (tid == 0) n_tiles_out[1 + g] = (need > 0 && k == need) ? moved_rows[g] : 0;
   }
   if (tid == 1023) *n_tiles_out = M;
 }
@@ -101,6 +111,8 @@ __device__ __forceinline__ int4 tile_entry(const int4* __restrict__ tiles, int m
 // rounds and a second launch runs each leftover tile cut into 2, 4 or 8
 // pieces, which keeps more CUs busy. Cutting by rows and columns leaves every
 // output's K accumulation order unchanged, so results do not depend on it.
+constexpr int cmax(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
+
 __device__ __forceinline__ int main_tile_end(int total, int G) {
   const int full = total / G * G;
   const int tail = total - full;
@@ -196,6 +208,59 @@ struct TailPieces {
   }
 };
 
+// Leftover tiles that are all short, with at most HMQ rows each (HMQ = BM/4
+// or BM/2): each is cut by columns only into SN pieces of HMQ rows by BN / SN
+// columns (unit u is column piece u % SN of tile main_tile_end + u / SN), so
+// no piece is empty and no duplicate token rows are staged. These pieces
+// stream weight slices with little math, so more of them in flight (more CUs,
+// up to five slice buffers each) is what makes them fast.
+template <int HMQ, int SN, int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF,
+          bool GA>
+struct TailShort {
+  static constexpr int HN = BN / SN;
+  static constexpr bool VALID = HN % (WN * MF) == 0;   // every wave keeps an MFMA column tile
+  static constexpr int BUF_BYTES =
+      TileGemmDL<HMQ, VALID ? HN : WN * MF, WM, WN, EPI, BK, MF, GA, 2>::LDS_BUF * 2;
+  static constexpr int NB = 160 * 1024 / BUF_BYTES;
+  using TG = TileGemmDL<HMQ, VALID ? HN : WN * MF, WM, WN, EPI, BK, MF, GA,
+                        NB >= 5 ? 5 : NB < 2 ? 2 : NB>;
+  __device__ static void run(const bf16* A, const int32_t* rows, const bf16* W, bf16* C,
+                             const int4* tiles, int n_m, int first, int left, int N, int K,
+                             int64_t w_stride, int n_n, int64_t ldc, const int32_t* o_tok,
+                             const int32_t* o_slot, int o_k, bf16* lds) {
+    if constexpr (VALID) {
+      const int units = SN * left;
+      const int nk = K / BK;
+      // consecutive units on consecutive workgroups, which the hardware deals
+      // round-robin to the XCDs: the pieces share little, so they should
+      // spread over every XCD's L2 and memory path rather than fill a few
+      const int slot = blockIdx.x;
+      auto get = [&](int i, GemmTile& t) -> bool {
+        for (int u = slot + i * (int)gridDim.x; u < units; u += gridDim.x) {
+          int mt, nt;
+          tile_coords<GROUP_M>(first + u / SN, n_m, n_n, mt, nt);
+          const int4 e = tile_entry(tiles, mt);
+          const int n0 = nt * BN + (u % SN) * HN;
+          if (n0 >= N) continue;
+          t.a = GA ? A : A + (int64_t)e.y * K;
+          t.rows = GA ? rows + e.y : nullptr;
+          t.a_rows = min(e.z - e.y, HMQ);
+          t.n0 = n0;
+          t.b = W + (int64_t)e.x * w_stride + (int64_t)n0 * K;
+          t.c_row = e.y;
+          t.nk = nk;
+          t.o_tok = o_tok;
+          t.o_slot = o_slot;
+          t.o_k = o_k;
+          return true;
+        }
+        return false;
+      };
+      TG::run_tiles(get, N, K, C, ldc, lds);
+    }
+  }
+};
+
 // The leftover tiles with the finest split S in {2, 4, 8} for which
 // S * leftover <= G (G: the main kernel's grid size, also this grid's).
 // Splitting by rows and columns leaves every output's K order unchanged.
@@ -204,19 +269,52 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ rows, const bf16* __restrict__ W,
     bf16* __restrict__ C, const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr,
     int N, int K, int64_t w_stride, int n_n, int64_t ldc, const int32_t* __restrict__ o_tok,
-    const int32_t* __restrict__ o_slot, int o_k, int G) {
+    const int32_t* __restrict__ o_slot, int o_k, int G, const int* __restrict__ short_rows) {
   using P2 = TailPieces<2, 1, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
   using P4 = TailPieces<2, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
   using P8 = TailPieces<4, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
-  constexpr int E2 = P2::TG::LDS_ELEMS, E4 = P4::TG::LDS_ELEMS, E8 = P8::TG::LDS_ELEMS;
-  constexpr int ELEMS = E2 > E4 ? (E2 > E8 ? E2 : E8) : (E4 > E8 ? E4 : E8);
+  // all-short leftovers: 64- or 128-row pieces, column quarters, halves or whole
+  using Q4 = TailShort<BM / 4, 4, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
+  using Q2 = TailShort<BM / 4, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
+  using Q1 = TailShort<BM / 4, 1, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
+  using H4 = TailShort<BM / 2, 4, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
+  using H2 = TailShort<BM / 2, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
+  using H1 = TailShort<BM / 2, 1, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
+  constexpr int ELEMS = cmax(cmax(P2::TG::LDS_ELEMS, P4::TG::LDS_ELEMS, P8::TG::LDS_ELEMS),
+                             cmax(Q4::TG::LDS_ELEMS, Q2::TG::LDS_ELEMS, Q1::TG::LDS_ELEMS),
+                             cmax(H4::TG::LDS_ELEMS, H2::TG::LDS_ELEMS, H1::TG::LDS_ELEMS));
   __shared__ __attribute__((aligned(1024))) bf16 lds[ELEMS];
   const int n_m = *n_mt_ptr;
   const int total = n_m * n_n;
   const int first = main_tile_end(total, G);
   const int left = total - first;
   if (left == 0) return;
-  if (8 * left <= G)
+  const int srows = short_rows ? *short_rows : 0;
+  if (srows > 0) {
+    // the finest valid column split with a piece per workgroup
+    const bool quarter = srows <= BM / 4;
+    if (Q4::VALID && 4 * left <= G) {
+      if (quarter)
+        Q4::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
+                o_k, lds);
+      else
+        H4::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
+                o_k, lds);
+    } else if (Q2::VALID) {
+      if (quarter)
+        Q2::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
+                o_k, lds);
+      else
+        H2::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
+                o_k, lds);
+    } else if (quarter) {
+      Q1::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
+              o_k, lds);
+    } else {
+      H1::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
+              o_k, lds);
+    }
+  } else if (8 * left <= G)
     P8::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot, o_k,
             lds);
   else if (4 * left <= G)
@@ -240,7 +338,7 @@ static hipError_t grouped_gemm_dl_launch(const bf16* A, const int32_t* rows, con
                                          bf16* C, const int4* tiles, const int* n_mt, int N,
                                          int K, int64_t w_stride, int64_t ldc,
                                          int64_t max_mtiles, int per_cu, hipStream_t s,
-                                         const int32_t* o_tok = nullptr,
+                                         const int* short_rows, const int32_t* o_tok = nullptr,
                                          const int32_t* o_slot = nullptr, int o_k = 0) {
   const int n_n = (N + BN - 1) / BN;
   const int G = gemm_grid(max_mtiles, n_n, per_cu);
@@ -251,7 +349,7 @@ static hipError_t grouped_gemm_dl_launch(const bf16* A, const int32_t* rows, con
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((grouped_gemm_tail_kernel<BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>),
                      dim3((unsigned)G), dim3(64 * WM * WN), 0, s, A, rows, W, C, tiles, n_mt, N,
-                     K, w_stride, n_n, ldc, o_tok, o_slot, o_k, (int)G);
+                     K, w_stride, n_n, ldc, o_tok, o_slot, o_k, (int)G, short_rows);
   return hipGetLastError();
 }
 
@@ -381,31 +479,33 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
     const int64_t s1 = (int64_t)w1_rows * d;
     if (swiglu && rows)
       err = grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_SWIGLU_BF16, 64, kGemmGroupM, 16, true>(
-          X, rows, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s);
+          X, rows, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s, n_mt + 1);
     else if (swiglu)
       err = grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_SWIGLU_BF16, 64, kGemmGroupM, 16>(
-          X, nullptr, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s);
+          X, nullptr, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s, n_mt + 1);
     else if (rows)
       err = grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_RELU_BF16, 64, kGemmGroupM, 16, true>(
-          X, rows, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s);
+          X, rows, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s, n_mt + 1);
     else
       err = grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_RELU_BF16, 64, kGemmGroupM, 16>(
-          X, nullptr, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s);
+          X, nullptr, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s, n_mt + 1);
     if (err != hipSuccess) return err;
     const bf16* W2 = (const bf16*)w2;
     bf16* Y = (bf16*)y_perm;
     const int64_t s2 = (int64_t)d * dff;
     if (o_tok && narrow2)
       return grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_SLOTS_BF16, 64, kGemmGroupM, 16>(
-          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, o_tok, o_slot, desc.k);
+          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2, o_tok, o_slot,
+          desc.k);
     if (o_tok)
       return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_SLOTS_BF16, 64, kGemmGroupM, 16>(
-          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, o_tok, o_slot, desc.k);
+          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2, o_tok, o_slot,
+          desc.k);
     if (narrow2)
       return grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_STORE_BF16, 64, kGemmGroupM, 16>(
-          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s);
+          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2);
     return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_STORE_BF16, 64, kGemmGroupM, 16>(
-        H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s);
+        H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2);
   }
   hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,
                      desc.max_rows, kF32BM, tiles, tiles2, n_mt, 0, 0, 0, 0, 1);
