@@ -171,10 +171,11 @@ struct TailPieces {
   static constexpr int BUF_BYTES = TileGemmDL<HM, HN, WM, WN, EPI, BK, MF, GA, 2>::LDS_BUF * 2;
   static constexpr int NB = 160 * 1024 / BUF_BYTES;
   using TG = TileGemmDL<HM, HN, WM, WN, EPI, BK, MF, GA, NB >= 5 ? 5 : NB < 2 ? 2 : NB>;
-  __device__ static void run(const bf16* A, const int32_t* rows, const bf16* W, bf16* C,
-                             const int4* tiles, int n_m, int first, int left, int N, int K,
-                             int64_t w_stride, int n_n, int64_t ldc, const int32_t* o_tok,
-                             const int32_t* o_slot, int o_k, bf16* lds) {
+  __device__ __forceinline__ static void run(const bf16* A, const int32_t* rows, const bf16* W,
+                                             bf16* C, const int4* tiles, int n_m, int first,
+                                             int left, int N, int K, int64_t w_stride, int n_n,
+                                             int64_t ldc, const int32_t* o_tok,
+                                             const int32_t* o_slot, int o_k, bf16* lds) {
     const int units = S * left;
     const int nk = K / BK;
     const int slot = xcd_virtual_id(blockIdx.x, gridDim.x, 0);
@@ -224,10 +225,11 @@ struct TailShort {
   static constexpr int NB = 160 * 1024 / BUF_BYTES;
   using TG = TileGemmDL<HMQ, VALID ? HN : WN * MF, WM, WN, EPI, BK, MF, GA,
                         NB >= 5 ? 5 : NB < 2 ? 2 : NB>;
-  __device__ static void run(const bf16* A, const int32_t* rows, const bf16* W, bf16* C,
-                             const int4* tiles, int n_m, int first, int left, int N, int K,
-                             int64_t w_stride, int n_n, int64_t ldc, const int32_t* o_tok,
-                             const int32_t* o_slot, int o_k, bf16* lds) {
+  __device__ __forceinline__ static void run(const bf16* A, const int32_t* rows, const bf16* W,
+                                             bf16* C, const int4* tiles, int n_m, int first,
+                                             int left, int N, int K, int64_t w_stride, int n_n,
+                                             int64_t ldc, const int32_t* o_tok,
+                                             const int32_t* o_slot, int o_k, bf16* lds) {
     if constexpr (VALID) {
       const int units = SN * left;
       const int nk = K / BK;
@@ -280,8 +282,17 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
   using H4 = TailShort<BM / 2, 4, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
   using H2 = TailShort<BM / 2, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
   using H1 = TailShort<BM / 2, 1, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
+  // 64-row pieces with K slices twice as deep (one barrier per two slices'
+  // worth of K: these pieces are paced by the per-slice round trip); the
+  // gathered-row path keeps its own slice depth
+  constexpr int BKW = GA ? BK : 2 * BK;
+  using W4 = TailShort<BM / 4, 4, BM, BN, WM, WN, EPI, BKW, GROUP_M, MF, GA>;
+  using W2 = TailShort<BM / 4, 2, BM, BN, WM, WN, EPI, BKW, GROUP_M, MF, GA>;
+  using W1 = TailShort<BM / 4, 1, BM, BN, WM, WN, EPI, BKW, GROUP_M, MF, GA>;
   constexpr int ELEMS = cmax(cmax(P2::TG::LDS_ELEMS, P4::TG::LDS_ELEMS, P8::TG::LDS_ELEMS),
-                             cmax(Q4::TG::LDS_ELEMS, Q2::TG::LDS_ELEMS, Q1::TG::LDS_ELEMS),
+                             cmax(cmax(Q4::TG::LDS_ELEMS, Q2::TG::LDS_ELEMS, Q1::TG::LDS_ELEMS),
+                                  cmax(W4::TG::LDS_ELEMS, W2::TG::LDS_ELEMS, W1::TG::LDS_ELEMS),
+                                  0),
                              cmax(H4::TG::LDS_ELEMS, H2::TG::LDS_ELEMS, H1::TG::LDS_ELEMS));
   __shared__ __attribute__((aligned(1024))) bf16 lds[ELEMS];
   const int n_m = *n_mt_ptr;
@@ -293,7 +304,18 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
   if (srows > 0) {
     // the finest valid column split with a piece per workgroup
     const bool quarter = srows <= BM / 4;
-    if (Q4::VALID && 4 * left <= G) {
+    const bool deep = !GA && K % BKW == 0;
+    if (quarter && deep) {
+      if (W4::VALID && 4 * left <= G)
+        W4::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
+                o_k, lds);
+      else if (W2::VALID)
+        W2::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
+                o_k, lds);
+      else
+        W1::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
+                o_k, lds);
+    } else if (Q4::VALID && 4 * left <= G) {
       if (quarter)
         Q4::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
                 o_k, lds);

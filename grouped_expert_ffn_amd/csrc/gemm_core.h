@@ -394,7 +394,7 @@ struct TileGemmDL {
     // (NBUF-2 whole slices, and the sub-steps around the barriers).
     // sched_barrier fences keep the compiler from moving MFMAs across the
     // slice barrier, which would leave the reads before it uncovered.
-    static_assert(NSUB == 2, "the loop below pipelines two sub-steps per slice");
+    static_assert(NSUB % 2 == 0, "the loop below alternates two fragment sets");
     using Yes = std::integral_constant<bool, true>;
     using No = std::integral_constant<bool, false>;
     // Wait until slice t, which the next barrier publishes, has landed from
@@ -435,7 +435,19 @@ struct TileGemmDL {
         read_b(cb, 0, b0);
 #pragma unroll
         for (int y = 0; y < TM; ++y) fy[y] = read_a(cb, 0, y);
-        step(Yes{}, b0, b1, cb, 1);
+        // sub-steps 0 .. NSUB-2 of the first slice, each reading the next
+        if constexpr (NSUB == 2) {
+          step(Yes{}, b0, b1, cb, 1);
+        } else {
+#pragma unroll
+          for (int j = 1; j < NSUB; ++j) {
+            if (j & 1)
+              step(Yes{}, b0, b1, cb, j);
+            else
+              step(Yes{}, b1, b0, cb, j);
+            if (j + 1 < NSUB) __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       // slice g fully read by this wave; slice g+1 landed from this wave (and
@@ -448,8 +460,19 @@ struct TileGemmDL {
         issue_next();                          // slice g+NBUF into the buffer g left
         if (busy) {
           step(Yes{}, b1, b0, nb, 0);          // last sub-step of g, reads g+1
-          __builtin_amdgcn_sched_barrier(0);
-          step(Yes{}, b0, b1, nb, 1);          // sub-step 0 of g+1, reads its sub-step 1
+          if constexpr (NSUB == 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            step(Yes{}, b0, b1, nb, 1);        // sub-step 0 of g+1, reads its sub-step 1
+          } else {
+#pragma unroll
+            for (int j = 1; j < NSUB; ++j) {   // sub-step j-1 of g+1, reads sub-step j
+              __builtin_amdgcn_sched_barrier(0);
+              if (j & 1)
+                step(Yes{}, b0, b1, nb, j);
+              else
+                step(Yes{}, b1, b0, nb, j);
+            }
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         wait_slice(gc + 2);                    // slice g+2 landed from this wave ...
