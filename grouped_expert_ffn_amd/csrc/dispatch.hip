@@ -397,6 +397,8 @@ int device_cu_count();
 // ---------------------------------------------------------------------------
 // 4. Row permute, token-major: one wave per token reads the row once in
 //    16-byte lanes and writes it to each of the token's materialised rows.
+//    U vectors per lane are held at once (U = 16: a whole 16 KiB row), so each
+//    destination row is written in one contiguous run.
 template <int U>
 __global__ __launch_bounds__(256) void permute_rows_kernel(const u32x4* __restrict__ h,
                                                            const int32_t* __restrict__ dest,
@@ -453,7 +455,7 @@ hipError_t launch_permute_rows(const void* h, const int32_t* dest, void* x_perm,
   if (T == 0) return hipSuccess;
   int64_t blocks = min((T + 3) / 4, (int64_t)device_cu_count() * 8);
   if (row_bytes % 16 == 0) {
-    hipLaunchKernelGGL(permute_rows_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s,
+    hipLaunchKernelGGL(permute_rows_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, s,
                        (const u32x4*)h, dest, (u32x4*)x_perm, T, k, row_bytes / 16);
   } else {
     hipLaunchKernelGGL(permute_rows_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
