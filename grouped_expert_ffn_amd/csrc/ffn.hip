@@ -108,9 +108,10 @@ __device__ __forceinline__ int4 tile_entry(const int4* __restrict__ tiles, int m
 
 // Tiles that do not fill a whole round of the persistent grid: when they
 // would occupy at most half of it, the main kernel stops after the whole
-// rounds and a second launch runs each leftover tile cut into 2, 4 or 8
-// pieces, which keeps more CUs busy. Cutting by rows and columns leaves every
-// output's K accumulation order unchanged, so results do not depend on it.
+// rounds and a second launch runs each leftover tile cut into pieces (rows
+// and columns, or columns only for short tiles), which keeps more CUs busy.
+// Cutting by rows and columns leaves every output's K accumulation order
+// unchanged, so results do not depend on it.
 constexpr int cmax(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
 
 __device__ __forceinline__ int main_tile_end(int total, int G) {
@@ -161,9 +162,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
 // each cut into S = SM * SN pieces of BM / SM rows by BN / SN columns: unit
 // u is piece u % S of tile main_tile_end + u / S. One piece per workgroup.
 // A piece has few MFMAs per K slice (fewer still on a short tile), so its
-// loop waits on memory latency rather than on the MFMAs: it keeps as many
-// slice buffers (up to five, four slices in flight) as fit in the 160 KiB of
-// LDS.
+// loop waits on memory rather than on the MFMAs: it keeps as many slice
+// buffers (up to five, four slices in flight) as fit in the 160 KiB of LDS.
 template <int SM, int SN, int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF,
           bool GA>
 struct TailPieces {
@@ -212,9 +212,9 @@ struct TailPieces {
 // Leftover tiles that are all short, with at most HMQ rows each (HMQ = BM/4
 // or BM/2): each is cut by columns only into SN pieces of HMQ rows by BN / SN
 // columns (unit u is column piece u % SN of tile main_tile_end + u / SN), so
-// no piece is empty and no duplicate token rows are staged. These pieces
-// stream weight slices with little math, so more of them in flight (more CUs,
-// up to five slice buffers each) is what makes them fast.
+// no piece is empty and fewer duplicate token rows are staged. These pieces
+// stream weight slices with little math; spreading them over more CUs and
+// XCDs is what makes them fast (deeper buffering beyond five slices is not).
 template <int HMQ, int SN, int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF,
           bool GA>
 struct TailShort {
@@ -282,9 +282,9 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
   using H4 = TailShort<BM / 2, 4, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
   using H2 = TailShort<BM / 2, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
   using H1 = TailShort<BM / 2, 1, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
-  // 64-row pieces with K slices twice as deep (one barrier per two slices'
-  // worth of K: these pieces are paced by the per-slice round trip); the
-  // gathered-row path keeps its own slice depth
+  // 64-row pieces with K slices twice as deep: half the barriers per K, which
+  // helps the few short pieces of a small layer; the gathered-row path keeps
+  // its own slice depth
   constexpr int BKW = GA ? BK : 2 * BK;
   using W4 = TailShort<BM / 4, 4, BM, BN, WM, WN, EPI, BKW, GROUP_M, MF, GA>;
   using W2 = TailShort<BM / 4, 2, BM, BN, WM, WN, EPI, BKW, GROUP_M, MF, GA>;
