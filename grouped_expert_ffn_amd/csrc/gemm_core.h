@@ -93,10 +93,10 @@ struct GemmTile {
 // next tile's first slices are already in flight while the current tile's
 // epilogue converts and stores its accumulators.
 //
-// A tile whose valid rows all fall in the lower half of the
-// wave grid (a_rows <= BM / 2 with two wave rows) leaves the upper waves
-// idle: they still fetch their share of each slice and meet every barrier,
-// but issue no MFMAs, so the lower waves have their SIMDs to themselves.
+// A tile whose valid rows all fall in the lower half of the wave grid
+// (a_rows <= BM / 2 with two wave rows) leaves the upper waves idle: they
+// still fetch their share of each slice and meet every barrier, but issue no
+// MFMAs, so the lower waves have their SIMDs to themselves.
 template <int BM, int BN, int WM, int WN, int EPI, int BK = 64, int MF = 16, bool GA = false,
           int NBUF = 2>
 struct TileGemmDL {
