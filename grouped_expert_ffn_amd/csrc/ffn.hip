@@ -40,10 +40,11 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
                                                         int4* __restrict__ tiles2,
                                                         int* __restrict__ n_tiles_out, int n_n1,
                                                         int G1, int n_n2, int G2, int group_m) {
-  __shared__ int scan_m[1024], scan_s[1024];
-  __shared__ int moved_rows[2];
-  const int tid = threadIdx.x;
-  if (tid < 2) moved_rows[tid] = 0;
+  // one thread per local expert (64 per wave); scans within a wave by
+  // shuffles, across waves through LDS
+  __shared__ int wsum_m[16], wsum_s[16], wmax[2][16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nw = (int)(blockDim.x >> 6);
   int r0 = 0, r1 = 0, mt = 0, sh = 0;
   if (tid < E_loc) {
     r0 = (int)min((int64_t)offsets[e_lo + tid], max_rows);
@@ -51,18 +52,29 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
     mt = r1 > r0 ? (r1 - r0 + BM - 1) / BM : 0;
     sh = (mt > 0 && r1 - r0 - (mt - 1) * BM <= BM / 2) ? 1 : 0;
   }
-  scan_m[tid] = mt;
-  scan_s[tid] = sh;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int am = tid >= o ? scan_m[tid - o] : 0;
-    const int as = tid >= o ? scan_s[tid - o] : 0;
-    __syncthreads();
-    scan_m[tid] += am;
-    scan_s[tid] += as;
-    __syncthreads();
+  int im = mt, is = sh;   // inclusive scans within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int am = __shfl_up(im, o), as = __shfl_up(is, o);
+    if (lane >= o) {
+      im += am;
+      is += as;
+    }
   }
-  const int M = scan_m[1023], S = scan_s[1023];
+  if (lane == 63) {
+    wsum_m[wv] = im;
+    wsum_s[wv] = is;
+  }
+  __syncthreads();
+  int M = 0, S = 0;
+  for (int w = 0; w < nw; ++w) {
+    if (w < wv) {
+      im += wsum_m[w];
+      is += wsum_s[w];
+    }
+    M += wsum_m[w];
+    S += wsum_s[w];
+  }
   for (int g = 0; g < 2; ++g) {
     const int n_n = g ? n_n2 : n_n1, G = g ? G2 : G1;
     int4* tab = g ? tiles2 : tiles1;
@@ -77,22 +89,32 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
       }
     }
     // short M-tiles j = 0..S-1 in expert order; those with j >= S - k move
-    const int j = scan_s[tid] - sh;   // short M-tiles of the experts before this one
+    const int j = is - sh;   // short M-tiles of the experts before this one
     const int mv = (sh && j >= S - k) ? 1 : 0;
     const int moved_before = max(0, j - (S - k));
-    const int start = scan_m[tid] - mt - moved_before;
+    const int start = im - mt - moved_before;
     for (int m = 0; m < mt - mv; ++m) {
       const int a = r0 + m * BM;
       tab[start + m] = make_int4(tid, a, min(a + BM, r1), 0);
     }
+    int rows_mv = 0;
     if (mv) {
       tab[M - k + j - (S - k)] = make_int4(tid, r0 + (mt - 1) * BM, r1, 0);
-      atomicMax(&moved_rows[g], r1 - r0 - (mt - 1) * BM);
+      rows_mv = r1 - r0 - (mt - 1) * BM;
     }
-    __syncthreads();
-    if (tid == 0) n_tiles_out[1 + g] = (need > 0 && k == need) ? moved_rows[g] : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) rows_mv = max(rows_mv, __shfl_xor(rows_mv, o));
+    if (lane == 0) wmax[g][wv] = (need > 0 && k == need) ? rows_mv : 0;
   }
-  if (tid == 1023) *n_tiles_out = M;
+  __syncthreads();
+  if (tid == 0) {
+    n_tiles_out[0] = M;
+    for (int g = 0; g < 2; ++g) {
+      int r = 0;
+      for (int w = 0; w < nw; ++w) r = max(r, wmax[g][w]);
+      n_tiles_out[1 + g] = r;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -467,6 +489,9 @@ int64_t gemm_max_mtiles(const moe_layer_desc_t& d) {
   return (rows + kF32BM - 1) / kF32BM + el;  // the smallest BM of any path
 }
 
+// threads of the tile-map launch: one per local expert, whole waves
+static unsigned tile_map_threads(int el) { return 64u * (unsigned)((max(el, 1) + 63) / 64); }
+
 // x_perm: the expert-ordered rows, or (gathered, rows != null) the token rows
 // h, read through rows = src_token. o_tok == null: grouped row r of the output
 // goes to row r of y_perm; otherwise to row o_tok[r] * k + o_slot[r].
@@ -492,8 +517,8 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
     // same either way
     const bool narrow2 = mt_ub * ((d + 255) / 256) < device_cu_count();
     const int n_n2 = narrow2 ? (d + 127) / 128 : (d + 255) / 256;
-    hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,
-                       desc.max_rows, kGemmBM, tiles, tiles2, n_mt, n_n1,
+    hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(tile_map_threads(el)), 0, s, offsets,
+                       e_lo, el, desc.max_rows, kGemmBM, tiles, tiles2, n_mt, n_n1,
                        gemm_grid(mt_ub, n_n1, 1), n_n2, gemm_grid(mt_ub, n_n2, 1), kGemmGroupM);
     const bf16* X = (const bf16*)x_perm;
     const bf16* W1 = (const bf16*)w1;
@@ -529,8 +554,8 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
     return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_STORE_BF16, 64, kGemmGroupM, 16>(
         H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2);
   }
-  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(1024), 0, s, offsets, e_lo, el,
-                     desc.max_rows, kF32BM, tiles, tiles2, n_mt, 0, 0, 0, 0, 1);
+  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(tile_map_threads(el)), 0, s, offsets, e_lo,
+                     el, desc.max_rows, kF32BM, tiles, tiles2, n_mt, 0, 0, 0, 0, 1);
   const float* X = (const float*)x_perm;
   float* H = (float*)act;
   if (swiglu)
