@@ -479,9 +479,9 @@ static hipError_t grouped_gemm_f32_launch(const float* A, const int32_t* a_rows,
 // GEMM1 (SwiGLU) stages 128 gate + 128 up weight rows per tile and writes
 // 128 activation columns; GEMM2 stages 256 weight rows (128 for small layers,
 // where wave tiles are 128 x 32). Tiles are walked
-// 4 M-tiles per N column (GROUP_M = 4) in XCD-major order.
+// 8 M-tiles per N column (GROUP_M = 8) in XCD-major order.
 constexpr int kGemmBM = 256;
-constexpr int kGemmGroupM = 4;
+constexpr int kGemmGroupM = 8;
 
 int64_t gemm_max_mtiles(const moe_layer_desc_t& d) {
   const int64_t el = d.E / d.ep_size;
