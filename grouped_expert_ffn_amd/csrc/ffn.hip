@@ -251,7 +251,8 @@ struct TailShort {
                                              bf16* C, const int4* tiles, int n_m, int first,
                                              int left, int N, int K, int64_t w_stride, int n_n,
                                              int64_t ldc, const int32_t* o_tok,
-                                             const int32_t* o_slot, int o_k, bf16* lds) {
+                                             const int32_t* o_slot, int o_k, bf16* lds,
+                                             bool nt_w) {
     if constexpr (VALID) {
       const int units = SN * left;
       const int nk = K / BK;
@@ -276,6 +277,7 @@ struct TailShort {
           t.o_tok = o_tok;
           t.o_slot = o_slot;
           t.o_k = o_k;
+          t.nt_w = nt_w;
           return true;
         }
         return false;
@@ -293,7 +295,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ rows, const bf16* __restrict__ W,
     bf16* __restrict__ C, const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr,
     int N, int K, int64_t w_stride, int n_n, int64_t ldc, const int32_t* __restrict__ o_tok,
-    const int32_t* __restrict__ o_slot, int o_k, int G, const int* __restrict__ short_rows) {
+    const int32_t* __restrict__ o_slot, int o_k, int G, const int* __restrict__ short_rows,
+    int nt_w) {
   using P2 = TailPieces<2, 1, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
   using P4 = TailPieces<2, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
   using P8 = TailPieces<4, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
@@ -330,33 +333,42 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
     if (quarter && deep) {
       if (W4::VALID && 4 * left <= G)
         W4::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
-                o_k, lds);
+                o_k, lds,
+                nt_w != 0);
       else if (W2::VALID)
         W2::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
-                o_k, lds);
+                o_k, lds,
+                nt_w != 0);
       else
         W1::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
-                o_k, lds);
+                o_k, lds,
+                nt_w != 0);
     } else if (Q4::VALID && 4 * left <= G) {
       if (quarter)
         Q4::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
-                o_k, lds);
+                o_k, lds,
+                nt_w != 0);
       else
         H4::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
-                o_k, lds);
+                o_k, lds,
+                nt_w != 0);
     } else if (Q2::VALID) {
       if (quarter)
         Q2::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
-                o_k, lds);
+                o_k, lds,
+                nt_w != 0);
       else
         H2::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
-                o_k, lds);
+                o_k, lds,
+                nt_w != 0);
     } else if (quarter) {
       Q1::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
-              o_k, lds);
+              o_k, lds,
+                nt_w != 0);
     } else {
       H1::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot,
-              o_k, lds);
+              o_k, lds,
+                nt_w != 0);
     }
   } else if (8 * left <= G)
     P8::run(A, rows, W, C, tiles, n_m, first, left, N, K, w_stride, n_n, ldc, o_tok, o_slot, o_k,
@@ -382,7 +394,8 @@ static hipError_t grouped_gemm_dl_launch(const bf16* A, const int32_t* rows, con
                                          bf16* C, const int4* tiles, const int* n_mt, int N,
                                          int K, int64_t w_stride, int64_t ldc,
                                          int64_t max_mtiles, int per_cu, hipStream_t s,
-                                         const int* short_rows, const int32_t* o_tok = nullptr,
+                                         const int* short_rows, bool nt_w,
+                                         const int32_t* o_tok = nullptr,
                                          const int32_t* o_slot = nullptr, int o_k = 0) {
   const int n_n = (N + BN - 1) / BN;
   const int G = gemm_grid(max_mtiles, n_n, per_cu);
@@ -393,7 +406,7 @@ static hipError_t grouped_gemm_dl_launch(const bf16* A, const int32_t* rows, con
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((grouped_gemm_tail_kernel<BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>),
                      dim3((unsigned)G), dim3(64 * WM * WN), 0, s, A, rows, W, C, tiles, n_mt, N,
-                     K, w_stride, n_n, ldc, o_tok, o_slot, o_k, (int)G, short_rows);
+                     K, w_stride, n_n, ldc, o_tok, o_slot, o_k, (int)G, short_rows, (int)nt_w);
   return hipGetLastError();
 }
 
@@ -516,6 +529,13 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
     // part of one round of the grid idle; the K order of every output is the
     // same either way
     const bool narrow2 = mt_ub * ((d + 255) / 256) < device_cu_count();
+    // The leftover launches stream the weights of short tiles once. When the
+    // local experts' weights cannot stay in the 256 MiB last-level cache
+    // between layers anyway, those loads go non-temporal, so that they leave
+    // the down GEMM's output there for the combine; smaller layers keep their
+    // weights cached.
+    const int64_t w_bytes = (int64_t)el * (w1_rows + dff) * d * 2;   // W1 and W2 per expert
+    const bool nt_w = w_bytes > (int64_t)256 << 20;
     const int n_n2 = narrow2 ? (d + 127) / 128 : (d + 255) / 256;
     hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(tile_map_threads(el)), 0, s, offsets,
                        e_lo, el, desc.max_rows, kGemmBM, tiles, tiles2, n_mt, n_n1,
@@ -526,33 +546,33 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
     const int64_t s1 = (int64_t)w1_rows * d;
     if (swiglu && rows)
       err = grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_SWIGLU_BF16, 64, kGemmGroupM, 16, true>(
-          X, rows, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s, n_mt + 1);
+          X, rows, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s, n_mt + 1, nt_w);
     else if (swiglu)
       err = grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_SWIGLU_BF16, 64, kGemmGroupM, 16>(
-          X, nullptr, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s, n_mt + 1);
+          X, nullptr, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s, n_mt + 1, nt_w);
     else if (rows)
       err = grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_RELU_BF16, 64, kGemmGroupM, 16, true>(
-          X, rows, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s, n_mt + 1);
+          X, rows, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s, n_mt + 1, nt_w);
     else
       err = grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_RELU_BF16, 64, kGemmGroupM, 16>(
-          X, nullptr, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s, n_mt + 1);
+          X, nullptr, W1, H, tiles, n_mt, dff, d, s1, dff, mt_ub, 1, s, n_mt + 1, nt_w);
     if (err != hipSuccess) return err;
     const bf16* W2 = (const bf16*)w2;
     bf16* Y = (bf16*)y_perm;
     const int64_t s2 = (int64_t)d * dff;
     if (o_tok && narrow2)
       return grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_SLOTS_BF16, 64, kGemmGroupM, 16>(
-          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2, o_tok, o_slot,
+          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2, nt_w, o_tok, o_slot,
           desc.k);
     if (o_tok)
       return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_SLOTS_BF16, 64, kGemmGroupM, 16>(
-          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2, o_tok, o_slot,
+          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2, nt_w, o_tok, o_slot,
           desc.k);
     if (narrow2)
       return grouped_gemm_dl_launch<kGemmBM, 128, 2, 4, EPI_STORE_BF16, 64, kGemmGroupM, 16>(
-          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2);
+          H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2, nt_w);
     return grouped_gemm_dl_launch<kGemmBM, 256, 2, 4, EPI_STORE_BF16, 64, kGemmGroupM, 16>(
-        H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2);
+        H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2, nt_w);
   }
   hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(tile_map_threads(el)), 0, s, offsets, e_lo,
                      el, desc.max_rows, kF32BM, tiles, tiles2, n_mt, 0, 0, 0, 0, 1);

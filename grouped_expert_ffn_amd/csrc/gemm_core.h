@@ -64,6 +64,10 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// Cache-policy operand of a buffer load on this GPU family: bit 1 marks the
+// access non-temporal.
+constexpr int kNonTemporal = 2;
+
 // s_waitcnt with vmcnt <= N and no wait on the other counters (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -85,6 +89,9 @@ struct GemmTile {
   const int32_t* o_tok;  // EPI_SLOTS_BF16 only: token and slot of each grouped row
   const int32_t* o_slot;
   int o_k;
+  // weight slices loaded non-temporal (no reuse expected in the last-level
+  // cache), so that they do not evict data a later kernel reads
+  bool nt_w = false;
 };
 
 // Persistent tile loop of one workgroup: run_tiles(get, ...) multiplies the
@@ -212,9 +219,14 @@ struct TileGemmDL {
           uint32_t o = off[i];
           if (GA && wave_a)
             o = o * (uint32_t)(K * 2) + (((wave * LPW + i) & 1) ? chunk_odd : chunk_even);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rs, (__attribute__((address_space(3))) void*)(base + i * L::RPL * BK), 16, o, ko, 0,
-              0);
+          if (!wave_a && t.nt_w)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(base + i * L::RPL * BK), 16, o, ko,
+                0, kNonTemporal);
+          else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(base + i * L::RPL * BK), 16, o, ko,
+                0, 0);
         }
         return;
       }
@@ -227,9 +239,14 @@ struct TileGemmDL {
         uint32_t o = off[i];
         if (GA && is_a[i])
           o = o * (uint32_t)(K * 2) + (((wave * LPW + i) & 1) ? chunk_odd : chunk_even);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            is_a[i] ? ra : rb, (__attribute__((address_space(3))) void*)(base + i * L::RPL * BK),
-            16, o, ko, 0, 0);
+        if (!is_a[i] && t.nt_w)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rb, (__attribute__((address_space(3))) void*)(base + i * L::RPL * BK), 16, o, ko, 0,
+              kNonTemporal);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              is_a[i] ? ra : rb, (__attribute__((address_space(3))) void*)(base + i * L::RPL * BK),
+              16, o, ko, 0, 0);
       }
     };
     // load cursor: the tile and slice fetched next
