@@ -129,37 +129,62 @@ __global__ __launch_bounds__(1024) void scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 3. Stable rank inside each tile (one wave per tile). 64 assignments at a
-//    time in (token, slot) order: lanes holding the same expert find each
-//    other by matching the expert id bit by bit with ballots; a lane's rank
-//    is the number of matching lanes below it, added to the expert's running
-//    position (the prefix over earlier tiles, then updated by the highest
-//    matching lane).
-__global__ __launch_bounds__(64) void rank_kernel(
+// 3. Stable rank inside each tile. The tile's assignments are cut into
+//    kRankWaves consecutive blocks, one per wave. Each wave first counts its
+//    block per expert (LDS integer atomics), so every wave knows where its
+//    block starts within each expert: the prefix over earlier tiles plus the
+//    counts of the blocks before it. Then each wave ranks its block 64
+//    assignments at a time in (token, slot) order: lanes holding the same
+//    expert find each other by matching the expert id bit by bit with
+//    ballots; a lane's rank is the number of matching lanes below it, added
+//    to the expert's running position (updated by the highest matching lane).
+constexpr int kRankWaves = 4;
+__global__ __launch_bounds__(64 * kRankWaves) void rank_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ tile_prefix,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ dest,
     int32_t* __restrict__ src_token, int32_t* __restrict__ src_slot, int64_t T, int E, int k,
     int ebits, int64_t capacity, int64_t max_rows) {
-  __shared__ int32_t run[kMaxE];
+  __shared__ int32_t run[kRankWaves][kMaxE];
   __shared__ int32_t off[kMaxE];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) {
-    run[e] = tile_prefix[(int64_t)blockIdx.x * E + e];
-    off[e] = offsets[e];
-  }
-  __syncthreads();
-  const int64_t a0 = (int64_t)blockIdx.x * kTokTile * k;
-  const int64_t a1 = min(T * k, a0 + (int64_t)kTokTile * k);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int q = 0; q < kRankWaves; ++q)
+    for (int e = threadIdx.x; e < E; e += 64 * kRankWaves) run[q][e] = 0;
+  for (int e = threadIdx.x; e < E; e += 64 * kRankWaves) off[e] = offsets[e];
+  const int64_t t0 = (int64_t)blockIdx.x * kTokTile * k;
+  const int64_t t1 = min(T * k, t0 + (int64_t)kTokTile * k);
+  // this wave's block: a whole number of 64-assignment steps
+  const int64_t per = (t1 - t0 + 64 * kRankWaves - 1) / (64 * kRankWaves) * 64;
+  const int64_t a0 = min(t1, t0 + w * per);
+  const int64_t a1 = min(t1, a0 + per);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // the tile's ids, loaded up front so the serial matching loop below never
-  // waits on global memory (at most kTokTile * kMaxK / 64 per lane)
-  constexpr int kMaxIt = kTokTile * kMaxK / 64;
+  // the block's ids, loaded up front so the serial matching loop below never
+  // waits on global memory
+  constexpr int kMaxIt = kTokTile * kMaxK / (64 * kRankWaves);
   int ids[kMaxIt];
 #pragma unroll
   for (int it = 0; it < kMaxIt; ++it) {
     const int64_t my = a0 + (int64_t)it * 64 + lane;
     ids[it] = my < a1 ? idx[my] : -1;
   }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < kMaxIt; ++it) {
+    const int e = ids[it];
+    if (e >= 0 && e < E) atomicAdd(&run[w][e], 1);
+  }
+  __syncthreads();
+  // counts -> each block's start position within each expert
+  for (int e = threadIdx.x; e < E; e += 64 * kRankWaves) {
+    int32_t p = tile_prefix[(int64_t)blockIdx.x * E + e];
+#pragma unroll
+    for (int q = 0; q < kRankWaves; ++q) {
+      const int32_t c = run[q][e];
+      run[q][e] = p;
+      p += c;
+    }
+  }
+  __syncthreads();
+  int32_t* wrun = run[w];
 #pragma unroll
   for (int it = 0; it < kMaxIt; ++it) {
     const int64_t a = a0 + (int64_t)it * 64;
@@ -177,10 +202,10 @@ __global__ __launch_bounds__(64) void rank_kernel(
     int pos = 0;
     if (valid) {
       const int rank = __popcll(peers & below);
-      const int base = run[e];
+      const int base = wrun[e];
       pos = base + rank;
       const bool leader = (peers >> lane) == 1ull;  // highest lane of its group
-      if (leader) run[e] = base + __popcll(peers);
+      if (leader) wrun[e] = base + __popcll(peers);
     }
     if (in) {
       int32_t d = -1;
@@ -387,7 +412,7 @@ hipError_t launch_dispatch_plan(const int32_t* idx, int32_t* tile_hist, int32_t*
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, tile_hist, n_tiles, E, capacity,
                      max_rows, counts, offsets, send_splits, send_displs, ep_size, flags);
   if (n_tiles > 0)
-    hipLaunchKernelGGL(rank_kernel, dim3(n_tiles), dim3(64), 0, s, idx, tile_hist, offsets,
+    hipLaunchKernelGGL(rank_kernel, dim3(n_tiles), dim3(64 * kRankWaves), 0, s, idx, tile_hist, offsets,
                        dest, src_token, src_slot, T, E, k, ebits, capacity, max_rows);
   return hipGetLastError();
 }
