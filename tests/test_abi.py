@@ -117,3 +117,23 @@ def test_gather_rejects_token_rows_beyond_32bit_offsets(G):
 def test_fp32_allows_any_width(G):
     desc = G.make_desc(64, 30, 4, 2, 50, "f32", "softmax", "relu")
     assert G.workspace_size(desc) > 0
+
+
+def test_missing_library_fails_loudly(G, monkeypatch):
+    """Without the built library the binding raises; nothing falls back to a
+    CPU path."""
+    monkeypatch.setattr(G, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libmoe_dispatch.so"))
+    with pytest.raises(ImportError, match="no CPU fallback"):
+        G._load()
+
+
+def test_product_code_never_reaches_the_oracle():
+    """The package (binding, build script, HIP sources) neither imports nor
+    names the oracle, so no call of the library can be answered by it."""
+    pkg = os.path.join(ROOT, "grouped_expert_ffn_amd")
+    files = [p for ext in ("py", "hip", "h", "cpp")
+             for p in glob.glob(os.path.join(pkg, "**", f"*.{ext}"), recursive=True)]
+    files += glob.glob(os.path.join(ROOT, "include", "*.h"))
+    assert files
+    for p in files:
+        assert not re.search(r"\boracle\b|moe_oracle", open(p).read()), p
