@@ -80,7 +80,9 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void router_skinny_kernel(
     const bf16x8 hv = *reinterpret_cast<const bf16x8*>(hp + ks * 32);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const bf16x8 wv = *reinterpret_cast<const bf16x8*>(wp + (int64_t)b * 16 * d + ks * 32);
+      // rows E..E_pad-1 of W_r^T are zero: their lanes skip the load
+      bf16x8 wv = {};
+      if (b * 16 + lr < E) wv = *reinterpret_cast<const bf16x8*>(wp + (int64_t)b * 16 * d + ks * 32);
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, hv, acc[b], 0, 0, 0);
     }
   }
