@@ -13,11 +13,20 @@ two MFMA GEMMs), per-stage figures, and the CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--skip-cpu-baseline]
-                    [--cold-steps N] [--gather] [--slots] [--ablation] [--dedup]
+                    [--warm-steps N] [--clock-steps N] [--gather] [--slots] [--ablation]
+                    [--dedup]
 
-After the timed steps, N more steps run one by one, each after a 512 MiB
-write that evicts the 256 MiB last-level cache (MALL); their event-timed
-median is reported as "cold_mall" beside (not in) the main figure.
+Each timed step runs right after a 512 MiB write that evicts the 256 MiB
+last-level cache (MALL), outside the step's events, so no step finds its
+inputs or weights left in the MALL by the one before; `value` is the batch's
+tokens over the summed event time of the K steps. After them, N steps back
+to back without the eviction are reported as "warm_mall", and the GFX clock
+is sampled while a further set of steps runs ("gpu_clock").
+
+Peaks: HBM 8 TB/s and dense bf16 MFMA 2.5 PFLOP/s, MI355X's published
+figures (2.5 PFLOP/s is 256 CUs x 4096 bf16 FLOP per clock at 2.4 GHz,
+2.5166 PFLOP/s before rounding, so fractions against the unrounded product
+read 0.7% lower).
 """
 from __future__ import annotations
 
@@ -99,6 +108,105 @@ def host_description():
     return model, blas
 
 
+def core_counts():
+    """Physical cores, logical CPUs, and the CPUs this process may run on
+    (a container or lease can hold fewer than the machine has)."""
+    phys = None
+    try:
+        import psutil
+        phys = psutil.cpu_count(logical=False)
+    except Exception:  # pragma: no cover
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        avail = None
+    return {"physical_cores": phys, "logical_cpus": os.cpu_count(),
+            "cpus_available_to_process": avail}
+
+
+def git_sha():
+    """The commit of the working tree, or, in a copy without .git, the one the
+    library was built from (recorded by the build)."""
+    import subprocess
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                           text=True, timeout=30)
+        if r.returncode == 0 and r.stdout.strip():
+            return {"git_sha": r.stdout.strip(), "source": "working tree"}
+    except (OSError, subprocess.SubprocessError):
+        pass
+    path = os.path.join(ROOT, "grouped_expert_ffn_amd", "_build", "build_info.json")
+    try:
+        info = json.load(open(path))
+        return {"git_sha": info.get("git_sha"), "git_dirty_at_build": info.get("git_dirty"),
+                "source": "recorded when the library was built"}
+    except (OSError, ValueError):
+        return {"git_sha": None, "source": "unavailable"}
+
+
+def env_record(torch):
+    rocm = None
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    rec = {"device": torch.cuda.get_device_name(), "torch": torch.__version__,
+           "hip": torch.version.hip, "rocm": rocm, "library_sha": library_sha()}
+    rec.update(git_sha())
+    return rec
+
+
+def gpu_clock_during(run, n_steps):
+    """GFX clock samples (MHz, amdsmi) taken while `run(n_steps)` layer steps
+    execute back to back: the steps are enqueued first, then the clock is
+    read until an event after them has completed."""
+    if n_steps <= 0:
+        return None
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        handle = handles[0]
+        # the device torch runs on, matched by PCI bus (amdsmi lists every GPU
+        # of the machine, whatever the process may see)
+        props = torch.cuda.get_device_properties(torch.cuda.current_device())
+        bus = getattr(props, "pci_bus_id", None)
+        if bus is not None and len(handles) > 1:
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)      # "dddd:bb:dd.f"
+                if int(bdf.split(":")[1], 16) == int(bus):
+                    handle = h
+                    break
+        read = lambda: amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)  # noqa
+        read()
+    except Exception as e:  # pragma: no cover - depends on the host's driver access
+        return {"error": f"{type(e).__name__}: {e}"}
+    torch.cuda.synchronize()
+    run(n_steps)
+    done = torch.cuda.Event()
+    done.record(torch.cuda.current_stream())
+    samples, info = [], None
+    t0 = time.perf_counter()
+    while not done.query():
+        info = read()
+        samples.append(float(info["clk"]))
+        time.sleep(0.001)
+    span = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:  # pragma: no cover
+        pass
+    if not samples:
+        return {"error": "the steps finished before the first sample"}
+    return {"gfx_mhz_median": float(np.median(samples)), "gfx_mhz_min": min(samples),
+            "gfx_mhz_max": max(samples), "samples": len(samples), "steps": n_steps,
+            "span_s": span, "max_clk_mhz": info.get("max_clk") if info else None,
+            "source": "amdsmi GFX clock, sampled while the steps ran"}
+
+
 def cpu_baseline(cfg, inp, capacity, sample_tokens, min_seconds):
     """The oracle, untouched, on the first `sample_tokens` tokens of the same
     workload (all expert weights), timed on the host cores; the sample is
@@ -121,10 +229,14 @@ def cpu_baseline(cfg, inp, capacity, sample_tokens, min_seconds):
         total += time.perf_counter() - t0
         runs += 1
     model, blas = host_description()
-    return {"value": Ts * runs / total, "unit": "routed tokens/s", "cores": int(cores),
-            "kind": "oracle", "cpu_model": model, "blas": blas,
+    rec = {"value": Ts * runs / total, "unit": "routed tokens/s", "cores": int(cores),
+           "cores_are": "BLAS threads the oracle's matrix products ran on (its other steps "
+                        "are single-threaded numpy)",
+           "kind": "oracle", "cpu_model": model, "blas": blas}
+    rec.update(core_counts())
+    return dict(rec, **{
             "sample": f"first {Ts} of {cfg.T} tokens of {cfg.name}, all expert weights, "
-                      f"float64 numpy oracle, {runs} run(s) in {total:.1f} s"}
+                      f"float64 numpy oracle, {runs} run(s) in {total:.1f} s"})
 
 
 def ablation_baselines(G, desc, x_perm, offsets, w1, w2, reps=5):
@@ -321,9 +433,11 @@ def main():
     ap.add_argument("--dedup", action="store_true",
                     help="also time expert-parallel packing with one send row per "
                          "(rank, token) pair and the local experts run from those rows")
-    ap.add_argument("--cold-steps", type=int, default=5,
-                    help="extra steps, each after a 512 MiB write that evicts the 256 MiB MALL, "
-                         "timed one by one with events (reported beside the main figure)")
+    ap.add_argument("--warm-steps", type=int, default=20,
+                    help="extra steps back to back without evicting the MALL, timed by the "
+                         "wall clock (reported beside the main figure)")
+    ap.add_argument("--clock-steps", type=int, default=40,
+                    help="extra steps run back to back while the GFX clock is sampled")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -378,11 +492,13 @@ def main():
         if ev is not None:
             ev[2].record(stream)
         if slots:
-            G.grouped_ffn_slots(desc, h, b.src_token, b.src_slot, b.offsets, w1, w2, y_slots, ws)
+            G.grouped_ffn_slots(desc, h, b.src_token, b.src_slot, b.offsets, w1, w2, y_slots, ws,
+                                flags=b.flags)
         elif gather:
-            G.grouped_ffn_gather(desc, h, b.src_token, b.offsets, w1, w2, b.y_perm, ws)
+            G.grouped_ffn_gather(desc, h, b.src_token, b.offsets, w1, w2, b.y_perm, ws,
+                                 flags=b.flags)
         else:
-            G.grouped_ffn(desc, b.x_perm, b.offsets, w1, w2, b.y_perm, ws)
+            G.grouped_ffn(desc, b.x_perm, b.offsets, w1, w2, b.y_perm, ws, flags=b.flags)
         if ev is not None:
             ev[3].record(stream)
         if slots:
@@ -392,38 +508,46 @@ def main():
         if ev is not None:
             ev[4].record(stream)
 
+    # Timed region: K steps, each right after a 512 MiB write that evicts the
+    # 256 MiB last-level cache (MALL), so every step starts with its inputs in
+    # HBM and none in the MALL. The write sits outside the step's events;
+    # the step time is the sum of the four stage intervals.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     b.flags.zero_()
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
+        flush.fill_(i & 0xff)
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        flush.fill_(i & 0xff)
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
     stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])  # ms
+    step_ms = stage.sum(axis=1)
 
-    # the same step with a cold last-level cache: a 512 MiB write before each
-    # step evicts the 256 MiB MALL (outside the events that time the step)
-    cold = None
-    if args.cold_steps > 0:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
-               for _ in range(args.cold_steps)]
-        for i in range(args.cold_steps):
-            flush.fill_(i & 0xff)
-            step(cev[i])
+    # the same steps back to back without the write (what stays in the MALL
+    # from one step to the next is reused), timed by the wall clock
+    warm = None
+    if args.warm_steps > 0:
+        wev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+               for _ in range(args.warm_steps)]
         torch.cuda.synchronize()
-        cst = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in cev])
-        cold = {"steps": args.cold_steps, "ms_per_step": float(np.median(cst.sum(axis=1))),
-                "route_ms": float(np.median(cst[:, 0])), "permute_ms": float(np.median(cst[:, 1])),
-                "grouped_ffn_ms": float(np.median(cst[:, 2])),
-                "combine_ms": float(np.median(cst[:, 3]))}
-        cold["tokens_per_s"] = cfg.T / (cold["ms_per_step"] / 1e3)
-        del flush
+        tw = time.perf_counter()
+        for i in range(args.warm_steps):
+            step(wev[i])
+        torch.cuda.synchronize()
+        tw = time.perf_counter() - tw
+        wst = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in wev])
+        warm = {"steps": args.warm_steps, "ms_per_step_wall": tw / args.warm_steps * 1e3,
+                "tokens_per_s_wall": cfg.T * args.warm_steps / tw,
+                "ms_per_step": float(wst.sum(axis=1).mean()),
+                "grouped_ffn_ms": float(np.median(wst[:, 2]))}
+    clock = gpu_clock_during(lambda n: [step() for _ in range(n)], args.clock_steps)
+    del flush
     st_ms = np.median(stage, axis=0)
     flags = int(b.flags.item())
     offs = b.offsets.cpu().numpy().astype(np.int64)
@@ -443,10 +567,10 @@ def main():
     peak = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
     achieved = flops / ffn_s / 1e12
     traffic = measured_traffic(cfg.name)
-    ms_per_step = wall / args.steps * 1e3
+    ms_per_step = float(step_ms.mean())
     out = {
         "metric": "routed tokens/sec per MoE layer (route+permute+FFN+combine)",
-        "value": cfg.T * args.steps / wall,
+        "value": cfg.T * args.steps / (step_ms.sum() / 1e3),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step,
@@ -473,9 +597,15 @@ def main():
             "rows_kept": n_kept, "rows_local": n_local, "flags": flags,
         },
         "routing": routing_report(cfg, b, capacity, eb),
-        "cold_mall": cold,
-        "env": {"device": torch.cuda.get_device_name(), "torch": torch.__version__,
-                "hip": torch.version.hip, "library_sha": library_sha()},
+        "timing": {"mall": "evicted before every timed step (512 MiB write outside the "
+                           "step's events)",
+                   "value_from": "sum of the timed steps' event durations",
+                   "step_ms_median": float(np.median(step_ms)),
+                   "step_ms_min": float(step_ms.min()), "step_ms_max": float(step_ms.max()),
+                   "wall_s_incl_evictions": wall},
+        "warm_mall": warm,
+        "gpu_clock": clock,
+        "env": env_record(torch),
     }
     if args.ablation:
         b_x = b.x_perm

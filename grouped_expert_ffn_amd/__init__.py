@@ -69,10 +69,10 @@ def _load():
         "moe_route": (I32, [D, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_topk_from_logits": (I32, [D, P, P, P, P, P]),
         "moe_permute": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
-        "moe_grouped_ffn": (I32, [D, P, P, P, P, P, P, SZ, P]),
-        "moe_grouped_ffn_gather": (I32, [D, P, P, P, P, P, P, P, SZ, P]),
+        "moe_grouped_ffn": (I32, [D, P, P, P, P, P, P, P, SZ, P]),
+        "moe_grouped_ffn_gather": (I32, [D, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_pack_dedup": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
-        "moe_grouped_ffn_slots": (I32, [D, P, P, P, P, P, P, P, P, SZ, P]),
+        "moe_grouped_ffn_slots": (I32, [D, P, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_combine_slots": (I32, [D, P, P, P, P, P, P]),
         "moe_unpermute_combine": (I32, [D, P, P, P, P, P, P]),
         "moe_layer_forward": (I32, [D, P, P, P, P, P, P, ctypes.POINTER(LayerBuffers), P, SZ, P]),
@@ -158,44 +158,56 @@ def _ws(ws):
     return _ptr(ws, "ws", torch.uint8), ctypes.c_size_t(ws.numel())
 
 
+def _flags(flags):
+    return _ptr(flags, "flags", torch.int32, (1,), optional=True)
+
+
 @dataclass
 class LayerBuffersT:
-    """Device tensors of every output and intermediate of the layer."""
-    logits: torch.Tensor
-    topk_idx: torch.Tensor
-    topk_gate: torch.Tensor
-    counts: torch.Tensor
-    offsets: torch.Tensor
-    dest: torch.Tensor
-    src_token: torch.Tensor
-    src_slot: torch.Tensor
-    send_splits: torch.Tensor
-    send_displs: torch.Tensor
-    x_perm: Optional[torch.Tensor]   # None: the fused call gathers rows from h
+    """Device tensors of the fused call's outputs and intermediates. Only
+    y_perm is required; a field left None is kept in the workspace (and
+    x_perm None also means the first expert GEMM gathers rows from h)."""
+    logits: Optional[torch.Tensor]
+    topk_idx: Optional[torch.Tensor]
+    topk_gate: Optional[torch.Tensor]
+    counts: Optional[torch.Tensor]
+    offsets: Optional[torch.Tensor]
+    dest: Optional[torch.Tensor]
+    src_token: Optional[torch.Tensor]
+    src_slot: Optional[torch.Tensor]
+    send_splits: Optional[torch.Tensor]
+    send_displs: Optional[torch.Tensor]
+    x_perm: Optional[torch.Tensor]
     y_perm: torch.Tensor
-    flags: torch.Tensor
+    flags: Optional[torch.Tensor]
 
 
-def alloc_buffers(desc: LayerDesc, device="cuda", x_perm=True) -> LayerBuffersT:
-    """Every buffer of the fused call; with x_perm=False the expert-ordered
-    copy of the rows is left out (the first expert GEMM then gathers them)."""
+def alloc_buffers(desc: LayerDesc, device="cuda", x_perm=True, outputs=True) -> LayerBuffersT:
+    """Buffers of the fused call. x_perm=False leaves out the expert-ordered
+    copy of the rows (the first expert GEMM then gathers them); outputs=False
+    leaves out every optional output (logits, routing, plan, splits, flags),
+    which the call then keeps in its workspace."""
     T, E, k, d, R = desc.T, desc.E, desc.k, desc.d, desc.max_rows
     dt = torch_dtype(desc)
     i32, f32 = torch.int32, torch.float32
+
+    def opt(make):
+        return make() if outputs else None
+
     return LayerBuffersT(
-        logits=torch.empty((T, E), dtype=f32, device=device),
-        topk_idx=torch.empty((T, k), dtype=i32, device=device),
-        topk_gate=torch.empty((T, k), dtype=f32, device=device),
-        counts=torch.empty((E,), dtype=i32, device=device),
-        offsets=torch.empty((E + 1,), dtype=i32, device=device),
-        dest=torch.empty((T, k), dtype=i32, device=device),
-        src_token=torch.full((max(R, 1),), -1, dtype=i32, device=device)[:R],
-        src_slot=torch.full((max(R, 1),), -1, dtype=i32, device=device)[:R],
-        send_splits=torch.empty((desc.ep_size,), dtype=torch.int64, device=device),
-        send_displs=torch.empty((desc.ep_size,), dtype=torch.int64, device=device),
+        logits=opt(lambda: torch.empty((T, E), dtype=f32, device=device)),
+        topk_idx=opt(lambda: torch.empty((T, k), dtype=i32, device=device)),
+        topk_gate=opt(lambda: torch.empty((T, k), dtype=f32, device=device)),
+        counts=opt(lambda: torch.empty((E,), dtype=i32, device=device)),
+        offsets=opt(lambda: torch.empty((E + 1,), dtype=i32, device=device)),
+        dest=opt(lambda: torch.empty((T, k), dtype=i32, device=device)),
+        src_token=opt(lambda: torch.full((max(R, 1),), -1, dtype=i32, device=device)[:R]),
+        src_slot=opt(lambda: torch.full((max(R, 1),), -1, dtype=i32, device=device)[:R]),
+        send_splits=opt(lambda: torch.empty((desc.ep_size,), dtype=torch.int64, device=device)),
+        send_displs=opt(lambda: torch.empty((desc.ep_size,), dtype=torch.int64, device=device)),
         x_perm=torch.empty((R, d), dtype=dt, device=device) if x_perm else None,
         y_perm=torch.empty((R, d), dtype=dt, device=device),
-        flags=torch.zeros((1,), dtype=torch.int32, device=device),
+        flags=opt(lambda: torch.zeros((1,), dtype=torch.int32, device=device)),
     )
 
 
@@ -249,7 +261,9 @@ def _w_shapes(desc):
     return (el, rows, desc.d), (el, desc.d, desc.d_ff)
 
 
-def grouped_ffn(desc, x_perm, offsets, w1, w2, y_perm, ws, stream=None):
+def grouped_ffn(desc, x_perm, offsets, w1, w2, y_perm, ws, stream=None, flags=None):
+    """flags: optional [1] int32 word, OR-ed with FLAG_ROW_OVERFLOW when local
+    rows lie past max_rows (the C argument before ws)."""
     dt = torch_dtype(desc)
     s1, s2 = _w_shapes(desc)
     R, d = desc.max_rows, desc.d
@@ -258,12 +272,14 @@ def grouped_ffn(desc, x_perm, offsets, w1, w2, y_perm, ws, stream=None):
         ctypes.byref(desc), _ptr(x_perm, "x_perm", dt, (R, d)),
         _ptr(offsets, "offsets", torch.int32, (desc.E + 1,)),
         _ptr(w1, "w1", dt, s1), _ptr(w2, "w2", dt, s2), _ptr(y_perm, "y_perm", dt, (R, d)),
-        wsp, wsn, _stream(stream)), "moe_grouped_ffn")
+        _flags(flags), wsp, wsn, _stream(stream)), "moe_grouped_ffn")
 
 
-def grouped_ffn_gather(desc, h, src_token, offsets, w1, w2, y_perm, ws, stream=None):
+def grouped_ffn_gather(desc, h, src_token, offsets, w1, w2, y_perm, ws, stream=None,
+                       flags=None):
     """h: the token rows [T, d], or a deduplicated send buffer [max_pairs, d]
-    (then src_token is the recv_rows of moe_pack_dedup)."""
+    (then src_token is the recv_rows of moe_pack_dedup). flags as for
+    grouped_ffn."""
     dt = torch_dtype(desc)
     s1, s2 = _w_shapes(desc)
     T, R, d = desc.T, desc.max_rows, desc.d
@@ -275,12 +291,13 @@ def grouped_ffn_gather(desc, h, src_token, offsets, w1, w2, y_perm, ws, stream=N
         _ptr(src_token, "src_token", torch.int32, (R,)),
         _ptr(offsets, "offsets", torch.int32, (desc.E + 1,)),
         _ptr(w1, "w1", dt, s1), _ptr(w2, "w2", dt, s2), _ptr(y_perm, "y_perm", dt, (R, d)),
-        wsp, wsn, _stream(stream)), "moe_grouped_ffn_gather")
+        _flags(flags), wsp, wsn, _stream(stream)), "moe_grouped_ffn_gather")
 
 
-def grouped_ffn_slots(desc, h, src_token, src_slot, offsets, w1, w2, y_slots, ws, stream=None):
+def grouped_ffn_slots(desc, h, src_token, src_slot, offsets, w1, w2, y_slots, ws, stream=None,
+                      flags=None):
     """Gathered first GEMM; the second writes each grouped row to its
-    (token, slot) row of y_slots [T*k, d]."""
+    (token, slot) row of y_slots [T*k, d]. flags as for grouped_ffn."""
     dt = torch_dtype(desc)
     s1, s2 = _w_shapes(desc)
     T, R, d, k = desc.T, desc.max_rows, desc.d, desc.k
@@ -291,7 +308,7 @@ def grouped_ffn_slots(desc, h, src_token, src_slot, offsets, w1, w2, y_slots, ws
         _ptr(src_slot, "src_slot", torch.int32, (R,)),
         _ptr(offsets, "offsets", torch.int32, (desc.E + 1,)),
         _ptr(w1, "w1", dt, s1), _ptr(w2, "w2", dt, s2), _ptr(y_slots, "y_slots", dt, (T * k, d)),
-        wsp, wsn, _stream(stream)), "moe_grouped_ffn_slots")
+        _flags(flags), wsp, wsn, _stream(stream)), "moe_grouped_ffn_slots")
 
 
 def max_pairs(desc) -> int:
@@ -345,20 +362,25 @@ def layer_forward(desc, h, w_router, bias, w1, w2, y, bufs: LayerBuffersT, ws, s
     dt = torch_dtype(desc)
     T, d, E, k, R = desc.T, desc.d, desc.E, desc.k, desc.max_rows
     s1, s2 = _w_shapes(desc)
+
+    def o(t, name, dtype, shape):
+        p = _ptr(t, name, dtype, shape, optional=True)
+        return None if p is None else p.value
+
     b = LayerBuffers(
-        logits=_ptr(bufs.logits, "logits", torch.float32, (T, E)).value,
-        topk_idx=_ptr(bufs.topk_idx, "topk_idx", torch.int32, (T, k)).value,
-        topk_gate=_ptr(bufs.topk_gate, "topk_gate", torch.float32, (T, k)).value,
-        counts=_ptr(bufs.counts, "counts", torch.int32, (E,)).value,
-        offsets=_ptr(bufs.offsets, "offsets", torch.int32, (E + 1,)).value,
-        dest=_ptr(bufs.dest, "dest", torch.int32, (T, k)).value,
-        src_token=_ptr(bufs.src_token, "src_token", torch.int32, (R,)).value,
-        src_slot=_ptr(bufs.src_slot, "src_slot", torch.int32, (R,)).value,
-        send_splits=_ptr(bufs.send_splits, "send_splits", torch.int64, (desc.ep_size,)).value,
-        send_displs=_ptr(bufs.send_displs, "send_displs", torch.int64, (desc.ep_size,)).value,
-        x_perm=(None if bufs.x_perm is None else _ptr(bufs.x_perm, "x_perm", dt, (R, d)).value),
+        logits=o(bufs.logits, "logits", torch.float32, (T, E)),
+        topk_idx=o(bufs.topk_idx, "topk_idx", torch.int32, (T, k)),
+        topk_gate=o(bufs.topk_gate, "topk_gate", torch.float32, (T, k)),
+        counts=o(bufs.counts, "counts", torch.int32, (E,)),
+        offsets=o(bufs.offsets, "offsets", torch.int32, (E + 1,)),
+        dest=o(bufs.dest, "dest", torch.int32, (T, k)),
+        src_token=o(bufs.src_token, "src_token", torch.int32, (R,)),
+        src_slot=o(bufs.src_slot, "src_slot", torch.int32, (R,)),
+        send_splits=o(bufs.send_splits, "send_splits", torch.int64, (desc.ep_size,)),
+        send_displs=o(bufs.send_displs, "send_displs", torch.int64, (desc.ep_size,)),
+        x_perm=o(bufs.x_perm, "x_perm", dt, (R, d)),
         y_perm=_ptr(bufs.y_perm, "y_perm", dt, (R, d)).value,
-        flags=_ptr(bufs.flags, "flags", torch.int32, (1,)).value)
+        flags=o(bufs.flags, "flags", torch.int32, (1,)))
     wsp, wsn = _ws(ws)
     _check(_lib.moe_layer_forward(
         ctypes.byref(desc), _ptr(h, "h", dt, (T, d)), _ptr(w_router, "w_router", dt, (d, E)),

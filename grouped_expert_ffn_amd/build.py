@@ -9,10 +9,12 @@ Every ``csrc/*.hip`` file is compiled to an object in parallel under
 from __future__ import annotations
 
 import glob
+import json
 import os
 import shutil
 import subprocess
 import sys
+import time
 from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -47,6 +49,27 @@ def _run(cmd):
     return out
 
 
+def _write_build_info():
+    """Record the git commit the library was built from (and whether the
+    tree had changes), so a copy of the tree without its .git directory can
+    still name the sources of its library."""
+    info = {"built_at": int(time.time()), "git_sha": None, "git_dirty": None}
+    root = os.path.dirname(PKG)
+    try:
+        sha = subprocess.run(["git", "-C", root, "rev-parse", "HEAD"], capture_output=True,
+                             text=True, timeout=30)
+        if sha.returncode == 0:
+            info["git_sha"] = sha.stdout.strip()
+            st = subprocess.run(["git", "-C", root, "status", "--porcelain", "--", "include",
+                                 "grouped_expert_ffn_amd/csrc"], capture_output=True, text=True,
+                                timeout=30)
+            info["git_dirty"] = bool(st.stdout.strip()) if st.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(os.path.join(BUILD, "build_info.json"), "w") as f:
+        json.dump(info, f)
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every HIP source for gfx950 and link the shared library.
     Always recompiles. Returns the library path."""
@@ -64,6 +87,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = LIB + ".tmp"
     outs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))
     os.replace(tmp, LIB)
+    _write_build_info()
     if verbose:
         for o in outs:
             if o.strip():

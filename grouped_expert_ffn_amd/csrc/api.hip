@@ -18,6 +18,39 @@ static int64_t max_pairs(const moe_layer_desc_t& d) {
 }
 static size_t dedup_scratch_ints(const moe_layer_desc_t& d);
 
+// The fused call's scratch copies of its optional outputs, in LayerScratch
+// order, each 256-byte aligned. Returns the bytes; with `ws` non-null also
+// carves the pointers from ws + offset.
+static size_t layer_scratch(const moe_layer_desc_t& d, char* base, LayerScratch* out) {
+  const size_t TE = (size_t)d.T * d.E, Tk = (size_t)d.T * d.k, R = (size_t)d.max_rows;
+  const size_t sizes[] = {TE * 4, Tk * 4, Tk * 4, (size_t)d.E * 4, ((size_t)d.E + 1) * 4,
+                          Tk * 4, R * 4, R * 4, (size_t)d.ep_size * 8, (size_t)d.ep_size * 8,
+                          4};
+  void* p[11];
+  size_t off = 0;
+  for (int i = 0; i < 11; ++i) {
+    p[i] = base ? base + off : nullptr;
+    off += align256(sizes[i]);
+  }
+  if (out) {
+    out->logits = (float*)p[0];
+    out->topk_idx = (int32_t*)p[1];
+    out->topk_gate = (float*)p[2];
+    out->counts = (int32_t*)p[3];
+    out->offsets = (int32_t*)p[4];
+    out->dest = (int32_t*)p[5];
+    out->src_token = (int32_t*)p[6];
+    out->src_slot = (int32_t*)p[7];
+    out->send_splits = (int64_t*)p[8];
+    out->send_displs = (int64_t*)p[9];
+    out->flags = (uint32_t*)p[10];
+  }
+  return off;
+}
+static size_t layer_scratch_bytes(const moe_layer_desc_t& d) {
+  return layer_scratch(d, nullptr, nullptr);
+}
+
 Workspace workspace_layout(const moe_layer_desc_t& d) {
   Workspace w{};
   size_t off = 0;
@@ -32,6 +65,8 @@ Workspace workspace_layout(const moe_layer_desc_t& d) {
   off += align256((size_t)d.max_rows * d.d_ff * elt_bytes(d.dtype));
   w.dedup = off;
   off += align256(dedup_scratch_ints(d) * 4);
+  w.layer = off;
+  off += layer_scratch_bytes(d);
   w.total = off;
   return w;
 }
@@ -154,14 +189,15 @@ static moe_status_t do_permute(const moe_layer_desc_t& d, const void* h, const i
 // rows == null: x holds the expert-ordered rows (x_perm); otherwise x is h and
 // row i of the grouped operand is h[rows[i]]
 // o_tok != null: grouped row r is written to row o_tok[r] * k + o_slot[r]
+// flags (may be null): OR-ed with ROW_OVERFLOW when local rows lie past max_rows
 static moe_status_t do_ffn(const moe_layer_desc_t& d, const void* x, const int32_t* rows,
                            const int32_t* offsets, const void* w1, const void* w2, void* y_perm,
-                           char* ws, hipStream_t s, const int32_t* o_tok = nullptr,
-                           const int32_t* o_slot = nullptr) {
+                           uint32_t* flags, char* ws, hipStream_t s,
+                           const int32_t* o_tok = nullptr, const int32_t* o_slot = nullptr) {
   const Workspace w = workspace_layout(d);
-  if (d.max_rows == 0) return MOE_OK;
   HIP_TRY(launch_grouped_ffn(d, x, rows, offsets, w1, w2, y_perm, ws + w.act,
-                             reinterpret_cast<int4*>(ws + w.gemm_tiles), s, o_tok, o_slot));
+                             reinterpret_cast<int4*>(ws + w.gemm_tiles), flags, s, o_tok,
+                             o_slot));
   return MOE_OK;
 }
 
@@ -249,21 +285,25 @@ MOE_EXPORT moe_status_t moe_permute(const moe_layer_desc_t* desc, const void* h,
 
 MOE_EXPORT moe_status_t moe_grouped_ffn(const moe_layer_desc_t* desc, const void* x_perm,
                                         const int32_t* offsets, const void* w1, const void* w2,
-                                        void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+                                        void* y_perm, uint32_t* flags, void* ws, size_t ws_bytes,
+                                        void* stream) {
   MOE_TRY(check_desc(desc));
   const moe_layer_desc_t& d = *desc;
   const int64_t R = d.max_rows, el = d.E / d.ep_size;
   const int64_t w1n = el * (d.act == MOE_ACT_SWIGLU ? 2 : 1) * d.d_ff * d.d, w2n = el * d.d * d.d_ff;
   MOE_TRY(check_bufs(desc, {{x_perm, R * d.d, true}, {y_perm, R * d.d, true}, {w1, w1n, true},
                             {w2, w2n, true}, {offsets, d.E + 1, false}}));
+  if (flags && ((uintptr_t)flags & 3u)) return MOE_ERR_ALIGN;
   MOE_TRY(check_ws(desc, ws, ws_bytes));
-  return do_ffn(*desc, x_perm, nullptr, offsets, w1, w2, y_perm, (char*)ws, (hipStream_t)stream);
+  return do_ffn(*desc, x_perm, nullptr, offsets, w1, w2, y_perm, flags, (char*)ws,
+                (hipStream_t)stream);
 }
 
 MOE_EXPORT moe_status_t moe_grouped_ffn_gather(const moe_layer_desc_t* desc, const void* h,
                                                const int32_t* src_token, const int32_t* offsets,
                                                const void* w1, const void* w2, void* y_perm,
-                                               void* ws, size_t ws_bytes, void* stream) {
+                                               uint32_t* flags, void* ws, size_t ws_bytes,
+                                               void* stream) {
   MOE_TRY(check_desc(desc));
   const moe_layer_desc_t& d = *desc;
   MOE_TRY(check_gather(d));
@@ -272,15 +312,16 @@ MOE_EXPORT moe_status_t moe_grouped_ffn_gather(const moe_layer_desc_t* desc, con
   MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {src_token, R, false},
                             {y_perm, R * d.d, true}, {w1, w1n, true}, {w2, w2n, true},
                             {offsets, d.E + 1, false}}));
+  if (flags && ((uintptr_t)flags & 3u)) return MOE_ERR_ALIGN;
   MOE_TRY(check_ws(desc, ws, ws_bytes));
-  return do_ffn(d, h, src_token, offsets, w1, w2, y_perm, (char*)ws, (hipStream_t)stream);
+  return do_ffn(d, h, src_token, offsets, w1, w2, y_perm, flags, (char*)ws, (hipStream_t)stream);
 }
 
 MOE_EXPORT moe_status_t moe_grouped_ffn_slots(const moe_layer_desc_t* desc, const void* h,
                                               const int32_t* src_token, const int32_t* src_slot,
                                               const int32_t* offsets, const void* w1,
-                                              const void* w2, void* y_slots, void* ws,
-                                              size_t ws_bytes, void* stream) {
+                                              const void* w2, void* y_slots, uint32_t* flags,
+                                              void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_desc(desc));
   const moe_layer_desc_t& d = *desc;
   MOE_TRY(check_gather(d));
@@ -289,9 +330,10 @@ MOE_EXPORT moe_status_t moe_grouped_ffn_slots(const moe_layer_desc_t* desc, cons
   MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {src_token, R, false}, {src_slot, R, false},
                             {y_slots, d.T * d.k * d.d, true}, {w1, w1n, true}, {w2, w2n, true},
                             {offsets, d.E + 1, false}}));
+  if (flags && ((uintptr_t)flags & 3u)) return MOE_ERR_ALIGN;
   MOE_TRY(check_ws(desc, ws, ws_bytes));
-  return do_ffn(d, h, src_token, offsets, w1, w2, y_slots, (char*)ws, (hipStream_t)stream,
-                src_token, src_slot);
+  return do_ffn(d, h, src_token, offsets, w1, w2, y_slots, flags, (char*)ws,
+                (hipStream_t)stream, src_token, src_slot);
 }
 
 MOE_EXPORT moe_status_t moe_combine_slots(const moe_layer_desc_t* desc, const void* y_slots,
@@ -349,36 +391,56 @@ MOE_EXPORT moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const vo
   MOE_TRY(check_desc(desc));
   if (!b) return MOE_ERR_NULL;
   const moe_layer_desc_t& d = *desc;
-  {
-    const int64_t TE = d.T * d.E, Tk = d.T * d.k, R = d.max_rows, el = d.E / d.ep_size;
-    const int64_t w1n = el * (d.act == MOE_ACT_SWIGLU ? 2 : 1) * d.d_ff * d.d;
-    const int64_t w2n = el * d.d * d.d_ff;
-    MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {w_router, (int64_t)d.d * d.E, true},
-                              {w1, w1n, true}, {w2, w2n, true}, {y, d.T * d.d, true},
-                              {b->x_perm, b->x_perm ? R * d.d : 0, true},
-                              {b->y_perm, R * d.d, true},
-                              {b->logits, TE, false}, {b->topk_idx, Tk, false},
-                              {b->topk_gate, Tk, false}, {b->counts, d.E, false},
-                              {b->offsets, d.E + 1, false}, {b->dest, Tk, false},
-                              {b->src_token, R, false}, {b->src_slot, R, false},
-                              {b->send_splits, d.ep_size, false},
-                              {b->send_displs, d.ep_size, false}, {b->flags, 1, false}}));
-  }
+  const int64_t TE = d.T * d.E, Tk = d.T * d.k, R = d.max_rows, el = d.E / d.ep_size;
+  const int64_t w1n = el * (d.act == MOE_ACT_SWIGLU ? 2 : 1) * d.d_ff * d.d;
+  const int64_t w2n = el * d.d * d.d_ff;
+  // required: inputs, y and y_perm; every other buffer may be NULL (a
+  // workspace copy stands in for it)
+  MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {w_router, (int64_t)d.d * d.E, true},
+                            {w1, w1n, true}, {w2, w2n, true}, {y, d.T * d.d, true},
+                            {b->y_perm, R * d.d, true}}));
+  auto opt = [&](const void* p, int64_t n, bool data) -> moe_status_t {
+    return p ? check_bufs(desc, {{p, n, data}}) : MOE_OK;
+  };
+  MOE_TRY(opt(b->x_perm, R * d.d, true));
+  MOE_TRY(opt(b->logits, TE, false));
+  MOE_TRY(opt(b->topk_idx, Tk, false));
+  MOE_TRY(opt(b->topk_gate, Tk, false));
+  MOE_TRY(opt(b->counts, d.E, false));
+  MOE_TRY(opt(b->offsets, d.E + 1, false));
+  MOE_TRY(opt(b->dest, Tk, false));
+  MOE_TRY(opt(b->src_token, R, false));
+  MOE_TRY(opt(b->src_slot, R, false));
+  MOE_TRY(opt(b->send_splits, d.ep_size, false));
+  MOE_TRY(opt(b->send_displs, d.ep_size, false));
+  MOE_TRY(opt(b->flags, 1, false));
   if (router_bias && ((uintptr_t)router_bias & 3u)) return MOE_ERR_ALIGN;
   if (!b->x_perm) MOE_TRY(check_gather(d));
   MOE_TRY(check_ws(desc, ws, ws_bytes));
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
-  MOE_TRY(do_route(d, h, w_router, router_bias, b->logits, b->topk_idx, b->topk_gate, b->flags,
-                   w, s));
-  MOE_TRY(do_permute(d, h, b->topk_idx, b->x_perm, b->counts, b->offsets, b->dest, b->src_token,
-                     b->src_slot, b->send_splits, b->send_displs, b->flags, w, s));
+  LayerScratch o;
+  layer_scratch(d, w + workspace_layout(d).layer, &o);
+  float* logits = b->logits ? b->logits : o.logits;
+  int32_t* idx = b->topk_idx ? b->topk_idx : o.topk_idx;
+  float* gate = b->topk_gate ? b->topk_gate : o.topk_gate;
+  int32_t* counts = b->counts ? b->counts : o.counts;
+  int32_t* offsets = b->offsets ? b->offsets : o.offsets;
+  int32_t* dest = b->dest ? b->dest : o.dest;
+  int32_t* src_token = b->src_token ? b->src_token : o.src_token;
+  int32_t* src_slot = b->src_slot ? b->src_slot : o.src_slot;
+  int64_t* splits = b->send_splits ? b->send_splits : o.send_splits;
+  int64_t* displs = b->send_displs ? b->send_displs : o.send_displs;
+  uint32_t* flags = b->flags ? b->flags : o.flags;
+  MOE_TRY(do_route(d, h, w_router, router_bias, logits, idx, gate, flags, w, s));
+  MOE_TRY(do_permute(d, h, idx, b->x_perm, counts, offsets, dest, src_token, src_slot, splits,
+                     displs, flags, w, s));
   // without x_perm the first expert GEMM gathers its rows from h
   if (b->x_perm)
-    MOE_TRY(do_ffn(d, b->x_perm, nullptr, b->offsets, w1, w2, b->y_perm, w, s));
+    MOE_TRY(do_ffn(d, b->x_perm, nullptr, offsets, w1, w2, b->y_perm, flags, w, s));
   else
-    MOE_TRY(do_ffn(d, h, b->src_token, b->offsets, w1, w2, b->y_perm, w, s));
-  return do_combine(d, b->y_perm, b->topk_idx, b->topk_gate, b->dest, y, s);
+    MOE_TRY(do_ffn(d, h, src_token, offsets, w1, w2, b->y_perm, flags, w, s));
+  return do_combine(d, b->y_perm, idx, gate, dest, y, s);
 }
 
 MOE_EXPORT const char* moe_status_str(moe_status_t st) {

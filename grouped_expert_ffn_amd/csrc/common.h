@@ -30,7 +30,25 @@ struct Workspace {
   size_t act;        // [max_rows, d_ff] dtype: SwiGLU/ReLU activations
   size_t dedup;      // deduplicated packing: pid, first_row [T,k]; pair_slot [pairs];
                      // counts [E], offsets [E+1], flags [1] (int32)
+  size_t layer;      // the fused call's own copies of the outputs its caller may
+                     // leave NULL (see LayerScratch)
   size_t total;
+};
+
+// Outputs of the fused layer call that its caller may pass as NULL, carved
+// from the workspace: each field is the caller's buffer or this scratch copy.
+struct LayerScratch {
+  float* logits;        // [T,E]
+  int32_t* topk_idx;    // [T,k]
+  float* topk_gate;     // [T,k]
+  int32_t* counts;      // [E]
+  int32_t* offsets;     // [E+1]
+  int32_t* dest;        // [T,k]
+  int32_t* src_token;   // [max_rows]
+  int32_t* src_slot;    // [max_rows]
+  int64_t* send_splits; // [ep_size]
+  int64_t* send_displs; // [ep_size]
+  uint32_t* flags;      // [1] (never read by the library, so never cleared)
 };
 
 // Scratch of the deduplicated packing, carved from the workspace.
@@ -81,7 +99,7 @@ hipError_t launch_combine(const void* y_perm, const int32_t* idx, const float* g
 hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
                               const int32_t* rows, const int32_t* offsets, const void* w1,
                               const void* w2, void* y_perm, void* act, int4* tiles,
-                              hipStream_t s, const int32_t* o_tok = nullptr,
+                              uint32_t* flags, hipStream_t s, const int32_t* o_tok = nullptr,
                               const int32_t* o_slot = nullptr);
 
 }  // namespace moe

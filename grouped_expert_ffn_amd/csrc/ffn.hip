@@ -39,12 +39,16 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
                                                         int BM, int4* __restrict__ tiles1,
                                                         int4* __restrict__ tiles2,
                                                         int* __restrict__ n_tiles_out, int n_n1,
-                                                        int G1, int n_n2, int G2, int group_m) {
+                                                        int G1, int n_n2, int G2, int group_m,
+                                                        uint32_t* __restrict__ flags) {
   // one thread per local expert (64 per wave); scans within a wave by
   // shuffles, across waves through LDS
   __shared__ int wsum_m[16], wsum_s[16], wmax[2][16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nw = (int)(blockDim.x >> 6);
+  // local rows past max_rows are not computed: report them
+  if (tid == 0 && flags && (int64_t)offsets[e_lo + E_loc] > max_rows)
+    atomicOr(flags, MOE_FLAG_ROW_OVERFLOW);
   int r0 = 0, r1 = 0, mt = 0, sh = 0;
   if (tid < E_loc) {
     r0 = (int)min((int64_t)offsets[e_lo + tid], max_rows);
@@ -511,7 +515,8 @@ static unsigned tile_map_threads(int el) { return 64u * (unsigned)((max(el, 1) +
 hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
                               const int32_t* rows, const int32_t* offsets, const void* w1,
                               const void* w2, void* y_perm, void* act, int4* tiles,
-                              hipStream_t s, const int32_t* o_tok, const int32_t* o_slot) {
+                              uint32_t* flags, hipStream_t s, const int32_t* o_tok,
+                              const int32_t* o_slot) {
   const int el = desc.E / desc.ep_size;
   const int e_lo = desc.ep_rank * el;
   const int64_t max_mt = gemm_max_mtiles(desc);
@@ -539,7 +544,8 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
     const int n_n2 = narrow2 ? (d + 127) / 128 : (d + 255) / 256;
     hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(tile_map_threads(el)), 0, s, offsets,
                        e_lo, el, desc.max_rows, kGemmBM, tiles, tiles2, n_mt, n_n1,
-                       gemm_grid(mt_ub, n_n1, 1), n_n2, gemm_grid(mt_ub, n_n2, 1), kGemmGroupM);
+                       gemm_grid(mt_ub, n_n1, 1), n_n2, gemm_grid(mt_ub, n_n2, 1), kGemmGroupM,
+                       flags);
     const bf16* X = (const bf16*)x_perm;
     const bf16* W1 = (const bf16*)w1;
     bf16* H = (bf16*)act;
@@ -575,7 +581,7 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
         H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2, nt_w);
   }
   hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(tile_map_threads(el)), 0, s, offsets, e_lo,
-                     el, desc.max_rows, kF32BM, tiles, tiles2, n_mt, 0, 0, 0, 0, 1);
+                     el, desc.max_rows, kF32BM, tiles, tiles2, n_mt, 0, 0, 0, 0, 1, flags);
   const float* X = (const float*)x_perm;
   float* H = (float*)act;
   if (swiglu)

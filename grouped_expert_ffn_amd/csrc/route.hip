@@ -236,6 +236,17 @@ __device__ __forceinline__ float bits_score(uint32_t b) {
   return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
 }
 
+// log sigmoid(s) - log sigmoid(s0) for s <= s0. log sigmoid(s) is
+// s - log(1 + e^s) below zero and -log(1 + e^-s) above; when both scores are
+// negative the differences s - s0 and of the two log terms are taken
+// separately, so the gap keeps full precision for large negative scores.
+__device__ __forceinline__ float log_sigmoid_gap(float s, float s0) {
+  if (s < 0.0f && s0 < 0.0f) return (s - s0) - (log1pf(expf(s)) - log1pf(expf(s0)));
+  const float ls = s < 0.0f ? s - log1pf(expf(s)) : -log1pf(expf(-s));
+  const float l0 = s0 < 0.0f ? s0 - log1pf(expf(s0)) : -log1pf(expf(-s0));
+  return ls - l0;
+}
+
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
@@ -345,9 +356,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     const float sum = seg_sum<W>(ex);
     g = ex / sum;
   } else {
-    const float sg = holder ? 1.0f / (1.0f + __expf(-my_v)) : 0.f;
-    const float sum = seg_sum<W>(sg);
-    g = sg / sum;
+    // logistic gates normalised over the chosen k, formed in the log domain:
+    // g_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) with l = log sigmoid(s) and
+    // slot 0 the top score, so scores far below zero (where sigmoid itself
+    // underflows in float32) still give finite gates
+    const float ex = holder ? __expf(log_sigmoid_gap(my_v, top)) : 0.f;
+    const float sum = seg_sum<W>(ex);
+    g = ex / sum;
   }
   if (holder) {
     idx[t * k + sl] = my_id;

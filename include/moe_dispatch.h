@@ -123,7 +123,12 @@ moe_status_t moe_route(const moe_layer_desc_t* desc, const void* h, const void* 
                        void* stream);
 
 /* Top-k and gates only, from caller logits [T,E] float32 (same rules as
- * moe_route). No workspace. */
+ * moe_route): the selection E_t = TopK(s_t, k) and the gates g_{t,e} of the
+ * repeatability page's token-choice formula, applied to scores the caller
+ * already holds (for instance scores replayed from a stored run, the page's
+ * route-replay passage). No workspace.
+ *   topk_idx [T,k] int32, topk_gate [T,k] float32 (written)
+ *   flags    [1] uint32, OR-ed with MOE_FLAG_NONFINITE_LOGIT */
 moe_status_t moe_topk_from_logits(const moe_layer_desc_t* desc, const float* logits,
                                   int32_t* topk_idx, float* topk_gate, uint32_t* flags,
                                   void* stream);
@@ -160,10 +165,16 @@ moe_status_t moe_permute(const moe_layer_desc_t* desc, const void* h, const int3
  * all ragged groups ("Dropless MoE Is a Runtime Problem as Much as a Model
  * Design", grouped GEMM paragraph). bf16 runs on MFMA with float32
  * accumulation; the SwiGLU product is formed in float32 and stored as bf16.
- *   w1 [E_loc, d_ff or 2*d_ff, d], w2 [E_loc, d, d_ff] (local experts only) */
+ *   w1 [E_loc, d_ff or 2*d_ff, d], w2 [E_loc, d, d_ff] (local experts only)
+ *   flags [1] uint32 or NULL: OR-ed with MOE_FLAG_ROW_OVERFLOW when the local
+ *         groups end past max_rows (offsets[e_hi] > max_rows, e_hi the first
+ *         expert after the local ones), i.e. when rows were not computed; the
+ *         same device-side overflow check as moe_permute (dropless page,
+ *         device-side metadata paragraph) for offsets a caller replays */
 moe_status_t moe_grouped_ffn(const moe_layer_desc_t* desc, const void* x_perm,
                              const int32_t* offsets, const void* w1, const void* w2,
-                             void* y_perm, void* ws, size_t ws_bytes, void* stream);
+                             void* y_perm, uint32_t* flags, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /* The same grouped expert FFN with dispatch fused into the first GEMM: row r
  * of an expert's group is read straight from h [T,d] at token src_token[r]
@@ -174,11 +185,11 @@ moe_status_t moe_grouped_ffn(const moe_layer_desc_t* desc, const void* x_perm,
  * expert-parallelism paragraph: fusing dispatch into the expert computation
  * removes an intermediate write and its read. Results are bit-identical to
  * moe_grouped_ffn on x_perm. bf16 needs T*min(k,ep_size)*d*2 bytes below
- * 4 GiB (MOE_ERR_SHAPE otherwise). */
+ * 4 GiB (MOE_ERR_SHAPE otherwise). flags as for moe_grouped_ffn. */
 moe_status_t moe_grouped_ffn_gather(const moe_layer_desc_t* desc, const void* h,
                                     const int32_t* src_token, const int32_t* offsets,
-                                    const void* w1, const void* w2, void* y_perm, void* ws,
-                                    size_t ws_bytes, void* stream);
+                                    const void* w1, const void* w2, void* y_perm,
+                                    uint32_t* flags, void* ws, size_t ws_bytes, void* stream);
 
 /* Both ends of the grouped expert FFN fused with the data movement around
  * it: the first GEMM reads token rows from h through src_token (as
@@ -190,11 +201,12 @@ moe_status_t moe_grouped_ffn_gather(const moe_layer_desc_t* desc, const void* h,
  * the same bits as y_perm[dest] of moe_grouped_ffn; rows of slots not
  * computed here (dropped, remote or past max_rows) are left untouched.
  * Needs the bf16 size limit of moe_grouped_ffn_gather (MOE_ERR_SHAPE
- * otherwise). */
+ * otherwise). flags as for moe_grouped_ffn. */
 moe_status_t moe_grouped_ffn_slots(const moe_layer_desc_t* desc, const void* h,
                                    const int32_t* src_token, const int32_t* src_slot,
                                    const int32_t* offsets, const void* w1, const void* w2,
-                                   void* y_slots, void* ws, size_t ws_bytes, void* stream);
+                                   void* y_slots, uint32_t* flags, void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /* Expert-parallel packing with token deduplication: one send row per
  * (destination rank, token) pair instead of one per (token, slot).
@@ -238,11 +250,14 @@ moe_status_t moe_combine_slots(const moe_layer_desc_t* desc, const void* y_slots
                                const int32_t* topk_idx, const float* topk_gate,
                                const int32_t* dest, void* y, void* stream);
 
-/* Buffers of the fused call; all are required device pointers with the
- * shapes given above, except x_perm, which may be NULL: then the fused call
- * makes only the plan in its permute step and the first expert GEMM reads
- * the rows from h (as moe_grouped_ffn_gather); x_perm is then not produced,
- * which also means no expert-parallel send buffer. */
+/* Buffers of the fused call, device pointers with the shapes given above.
+ * Only y_perm is required. Every other field may be NULL: the call then
+ * keeps that intermediate in its workspace (moe_workspace_size includes
+ * room for all of them) and the caller does not receive it. A NULL x_perm
+ * also changes the path: the permute step makes only the plan and the
+ * first expert GEMM reads the rows from h (as moe_grouped_ffn_gather), so
+ * no expert-parallel send buffer is produced. A NULL flags word means no
+ * overflow report. */
 typedef struct moe_layer_buffers {
   float* logits;        /* [T,E] */
   int32_t* topk_idx;    /* [T,k] */
@@ -259,10 +274,18 @@ typedef struct moe_layer_buffers {
   uint32_t* flags;      /* [1], caller-zeroed */
 } moe_layer_buffers_t;
 
-/* The whole layer in one call: route, permute, grouped FFN, unpermute +
- * combine, enqueued back to back on `stream` with no host synchronisation.
- * Equivalent to the four stage calls in order (with buffers->x_perm NULL:
- * moe_permute without x_perm, then moe_grouped_ffn_gather). */
+/* The whole layer in one call: y_t = sum over e in TopK(h_t W_r, k) of
+ * g_{t,e} f_e(h_t) (the repeatability page's token-choice formula), run as
+ * the staged path of the dispatch page ("Follow one documented dispatch and
+ * return path"): route, permute, grouped FFN, unpermute + combine, enqueued
+ * back to back on `stream` with no host synchronisation. Equivalent to the
+ * four stage calls in order (with buffers->x_perm NULL: moe_permute without
+ * x_perm, then moe_grouped_ffn_gather).
+ *   h [T,d], w_router [d,E], router_bias [E] float32 or NULL, w1, w2 as for
+ *   moe_grouped_ffn, y [T,d] (written; excludes the residual)
+ *   buffers: required (non-NULL), with the optional fields described above
+ * Errors: as the stage calls; MOE_ERR_NULL when buffers, buffers->y_perm or
+ * a required input is NULL. */
 moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const void* h, const void* w_router,
                                const float* router_bias, const void* w1, const void* w2, void* y,
                                const moe_layer_buffers_t* buffers, void* ws, size_t ws_bytes,

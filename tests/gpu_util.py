@@ -115,3 +115,69 @@ def run_layer(G, desc, dv, bufs=None, ws=None, y=None):
     G.layer_forward(desc, dv["h"], dv["w_router"], dv["bias"], dv["w1"], dv["w2"], y, bufs, ws)
     torch.cuda.synchronize()
     return y, bufs, ws
+
+
+def sample_tokens(T, n, seed, always=()):
+    """n distinct random tokens plus the given ones, sorted."""
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(T, size=min(n, T), replace=False).tolist() if T else []
+    return sorted(set(pick) | {t for t in always if 0 <= t < T})
+
+
+def edge_rows(offsets, e_lo, e_hi, max_rows, bm=256, short_all=128, per_edge=8, seed=0):
+    """Grouped rows at the edges of each local expert's 256-row M-tiles: the
+    first rows of its first tile, and the rows of its last tile (all of them
+    when that tile holds at most `short_all` rows, which is what makes it a
+    short tile, the kind the GEMMs run on half their waves and move into the
+    leftover launch; else `per_edge` from each end and a few inside)."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    offs = np.asarray(offsets, np.int64)
+    for e in range(e_lo, e_hi):
+        r0, r1 = min(int(offs[e]), max_rows), min(int(offs[e + 1]), max_rows)
+        if r1 <= r0:
+            continue
+        rows.update(range(r0, min(r1, r0 + per_edge)))
+        mt = (r1 - r0 + bm - 1) // bm
+        t0 = r0 + (mt - 1) * bm
+        if r1 - t0 <= short_all:
+            rows.update(range(t0, r1))
+        else:
+            rows.update(range(t0, t0 + per_edge))
+            rows.update(range(r1 - per_edge, r1))
+            rows.update(rng.integers(t0, r1, per_edge).tolist())
+    return sorted(rows)
+
+
+def check_tokens_vs_oracle(cfg, inp, y, idx_gpu, toks, capacity=-1, what="y", T=None):
+    """y[toks] against the per-token oracle y_t = sum over kept e of
+    g_{t,e} f_e(h_t), evaluated on the GPU's routing (route replay) with the
+    oracle's own float64 scores for the gates."""
+    T = cfg.T if T is None else T
+    toks = list(toks)
+    if not toks:
+        return (0.0, 0.0)
+    want = O.brute_force_tokens(inp["h"][:T], inp["w_router"], inp.get("bias"), inp["w1"],
+                                inp["w2"], toks, k=cfg.k, gate=cfg.gate, act=cfg.act,
+                                capacity=capacity, ep_size=cfg.ep_size, ep_rank=cfg.ep_rank,
+                                route_idx=idx_gpu)
+    got = host(y[torch.as_tensor(toks, device="cuda")])
+    return assert_close(got, want, TOL[cfg.dtype], what)
+
+
+def check_rows_vs_oracle(cfg, inp, y_rows, rows, src_token, offsets, what="y_perm rows"):
+    """Expert outputs of grouped rows against the oracle's f_e on the token
+    each row holds (the local expert owning row r is the one whose range
+    offsets[e]..offsets[e+1] contains r)."""
+    rows = np.asarray(rows, np.int64)
+    if rows.size == 0:
+        return (0.0, 0.0)
+    offs = np.asarray(offsets, np.int64)
+    e_of = np.searchsorted(offs, rows, side="right") - 1
+    lo = cfg.ep_rank * (cfg.E // cfg.ep_size)
+    want = np.zeros((rows.size, cfg.d))
+    for e in np.unique(e_of):
+        m = e_of == e
+        want[m] = O.expert_ffn(inp["h"][np.asarray(src_token)[rows[m]]], inp["w1"][e - lo],
+                               inp["w2"][e - lo], cfg.act)
+    return assert_close(np.asarray(y_rows, np.float64), want, TOL[cfg.dtype], what)

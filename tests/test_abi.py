@@ -108,10 +108,59 @@ def test_gather_rejects_token_rows_beyond_32bit_offsets(G):
     p = ctypes.c_void_p
     big = G.make_desc(1 << 19, 4096, 8, 2, 128, "bf16", "softmax", "swiglu")
     st = lib.moe_grouped_ffn_gather(ctypes.byref(big), p(1024), p(2048), p(4096), p(8192),
-                                    p(16384), p(32768), p(65536), 1 << 40, None)
+                                    p(16384), p(32768), None, p(65536), 1 << 40, None)
     assert st == 2
     assert lib.moe_grouped_ffn_gather(None, p(1024), p(2048), p(4096), p(8192), p(16384),
-                                      p(32768), p(65536), 1 << 40, None) == 1
+                                      p(32768), None, p(65536), 1 << 40, None) == 1
+
+
+def test_grouped_ffn_flags_word_is_optional_but_checked(G):
+    """moe_grouped_ffn's flags word may be NULL; a misaligned one is refused
+    before anything is enqueued."""
+    lib = G._lib
+    p = ctypes.c_void_p
+    desc = G.make_desc(64, 128, 8, 2, 128, "bf16", "softmax", "swiglu")
+    args = [p(1024), p(2048), p(4096), p(8192), p(16384)]
+    assert lib.moe_grouped_ffn(ctypes.byref(desc), *args, p(1026), p(1 << 20), 1 << 30, None) == 3
+    # NULL flags passes the argument checks (then the missing workspace is reported)
+    assert lib.moe_grouped_ffn(ctypes.byref(desc), *args, None, None, 0, None) == 6
+
+
+def _layer_call(G, desc, bufs, ws=None, ws_bytes=0):
+    p = ctypes.c_void_p
+    return G._lib.moe_layer_forward(ctypes.byref(desc), p(1 << 12), p(1 << 13), None,
+                                    p(1 << 14), p(1 << 15), p(1 << 16),
+                                    None if bufs is None else ctypes.byref(bufs),
+                                    p(ws), ws_bytes, None)
+
+
+def test_layer_forward_optional_outputs(G):
+    """Every buffer of the fused call but y_perm may be NULL (the workspace
+    holds those intermediates); a NULL buffers struct or y_perm is refused,
+    and a given optional buffer is still checked. All before any launch."""
+    desc = G.make_desc(64, 128, 8, 2, 128, "bf16", "softmax", "swiglu")
+    assert _layer_call(G, desc, None) == 1
+    b = G.LayerBuffers()                       # every field NULL
+    assert _layer_call(G, desc, b) == 1        # y_perm is required
+    b.y_perm = 1 << 20
+    assert _layer_call(G, desc, b) == 6        # only the workspace is missing now
+    b.logits = 1 << 21 | 2                     # a given buffer must be aligned
+    assert _layer_call(G, desc, b) == 3
+    b.logits = None
+    b.x_perm = 1 << 22 | 8                     # bf16 rows need 16-byte alignment
+    assert _layer_call(G, desc, b) == 3
+
+
+def test_workspace_holds_the_fused_calls_optional_outputs(G):
+    """The workspace has room for every optional output of the fused call:
+    logits [T,E] f32, ids, gates and dest [T,k], the inverse map [max_rows]
+    twice, counts, offsets, splits and a flag word."""
+    T, E, k = 32768, 256, 8
+    desc = G.make_desc(T, 7168, E, k, 2048, "bf16", "sigmoid_topk_renorm", "swiglu",
+                       ep_size=8)
+    need = T * E * 4 + 3 * T * k * 4 + 2 * T * k * 4
+    act = T * k * 2048 * 2
+    assert G.workspace_size(desc) >= act + need
 
 
 def test_fp32_allows_any_width(G):

@@ -127,3 +127,29 @@ def test_unpermute_combine(dtype, E, k, ep):
     el = E // ep[0]
     ref = O.unpermute_combine(yp, idx, gate, plan["dest"], ep[1] * el, (ep[1] + 1) * el)
     assert_close(host(y), ref, TOL[dtype] if dtype == "bf16" else 1e-6, "combine")
+
+
+def test_grouped_ffn_reports_rows_past_max_rows():
+    """A replayed offsets table whose local groups end past max_rows: the
+    rows that fit are computed, the rest are not, and ROW_OVERFLOW is set in
+    the flags word; a table that fits leaves the word clear, and groups of
+    other ranks past max_rows do not count."""
+    G = lib()
+    rng = np.random.default_rng(21)
+    d, dff = 128, 128
+    w1 = dev(_rand(rng, (2, 2 * dff, d), d ** -0.5, "bf16"), torch.bfloat16)
+    w2 = dev(_rand(rng, (2, d, dff), dff ** -0.5, "bf16"), torch.bfloat16)
+    x = dev(_rand(rng, (300, d), 1.0, "bf16"), torch.bfloat16)
+    for offsets, R, ep, rank, want in (([0, 100, 300], 200, 1, 0, True),
+                                       ([0, 100, 300], 300, 1, 0, False),
+                                       ([0, 100, 150, 250, 300], 160, 2, 0, False),
+                                       ([0, 100, 150, 250, 300], 260, 2, 1, True)):
+        E = len(offsets) - 1
+        desc = G.make_desc(R, d, E, 1, dff, "bf16", "softmax", "swiglu", ep_size=ep,
+                           ep_rank=rank, max_rows=R)
+        fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+        y = torch.zeros((R, d), dtype=torch.bfloat16, device="cuda")
+        G.grouped_ffn(desc, x[:R].contiguous(), dev(np.array(offsets, np.int32)), w1, w2, y,
+                      G.alloc_workspace(desc), flags=fl)
+        torch.cuda.synchronize()
+        assert bool(int(host(fl)[0]) & G.FLAG_ROW_OVERFLOW) == want, (offsets, R, ep, rank)

@@ -70,3 +70,40 @@ def test_random_layout_matches_oracle_and_per_expert_bits(seed):
                   w1b[e:e + 1].contiguous(), w2b[e:e + 1].contiguous(), hi - lo, d, dff, 1, act)
         torch.cuda.synchronize()
         assert torch.equal(ye, y[lo:hi]), f"seed {seed}: expert {e} differs when run alone"
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_leftover_pieces_with_streamed_weights(seed):
+    """Twelve experts at d = 1024, d_ff = 4096 hold 302 MB of weights, more
+    than the 256 MiB last-level cache, so the leftover launch loads its weight
+    slices non-temporal; random ragged groups with short last tiles put tiles
+    there. Outputs against the oracle, and each expert's bits against that
+    expert run alone (whose weights fit the cache: the other load policy)."""
+    G = lib()
+    rng = np.random.default_rng(7000 + seed)
+    el, d, dff, act = 12, 1024, 4096, "swiglu"
+    # full row tiles per expert; the row-tile count M is nudged to 1..4 mod 8,
+    # so the SwiGLU GEMM's 32 column tiles per row tile leave 32..128 tiles
+    # after its last whole round of 256 workgroups: the leftover launch
+    q = rng.integers(0, 3, el)
+    i = 0
+    while (el + int(q.sum())) % 8 not in (1, 2, 3, 4):
+        q[i % el] += 1
+        i += 1
+    sizes = [int(v) for v in 256 * q + rng.integers(1, 129, el)]
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(offsets[-1])
+    say(f"streamed-weights seed {seed}: rows {rows}, sizes {sizes}")
+    xb = dev((rng.standard_normal((rows, d))).astype(np.float32), torch.bfloat16)
+    w1b = dev((rng.standard_normal((el, 2 * dff, d)) * d ** -0.5).astype(np.float32), torch.bfloat16)
+    w2b = dev((rng.standard_normal((el, d, dff)) * dff ** -0.5).astype(np.float32), torch.bfloat16)
+    y = _run(G, xb, offsets, w1b, w2b, rows, d, dff, el, act)
+    torch.cuda.synchronize()
+    ref = O.grouped_ffn(host(xb), offsets, host(w1b), host(w2b), act, 0, el, rows)
+    assert_close(host(y), ref, TOL["bf16"], f"streamed weights seed {seed}")
+    for e in range(el):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        ye = _run(G, xb[lo:hi].contiguous(), np.array([0, hi - lo], np.int32),
+                  w1b[e:e + 1].contiguous(), w2b[e:e + 1].contiguous(), hi - lo, d, dff, 1, act)
+        torch.cuda.synchronize()
+        assert torch.equal(ye, y[lo:hi]), f"seed {seed}: expert {e} differs when run alone"

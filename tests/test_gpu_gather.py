@@ -7,7 +7,8 @@ import pytest
 import torch
 
 from oracle import moe_oracle as O
-from tests.gpu_util import TOL, assert_close, host, lib, run_layer, say, upload_layer
+from tests.gpu_util import (TOL, assert_close, check_rows_vs_oracle, check_tokens_vs_oracle, host,
+                            lib, run_layer, sample_tokens, say, upload_layer)
 from workloads import CONFIGS, make_inputs, small_layer_config
 
 pytestmark = pytest.mark.gpu
@@ -45,6 +46,11 @@ def test_fused_call_without_x_perm_is_bit_identical(name):
         lo, hi = host(b_a.offsets)[[cfg.ep_rank * el, (cfg.ep_rank + 1) * el]]
         hi = min(int(hi), desc.max_rows)
         assert torch.equal(b_a.y_perm[lo:hi], b_g.y_perm[lo:hi]), "local y_perm rows"
+        # and the gathered path's output against the oracle
+        toks = sample_tokens(cfg.T, 96, cfg.T, (0, cfg.T - 1))
+        err = check_tokens_vs_oracle(cfg, inp, y_g, host(b_g.topk_idx), toks, cap,
+                                     f"gathered y {name}")
+        say(f"  oracle on {len(toks)} tokens: max abs/rel err {err}")
 
 
 def test_gather_stage_call_matches_grouped_ffn_and_oracle():
@@ -102,8 +108,10 @@ def test_fused_call_without_x_perm_full_mixtral_layer():
     cfg = CONFIGS["mixtral_bf16"]
     inp = make_inputs(cfg)
     desc, dv = upload_layer(G, cfg, inp)
-    (y_a, _), (y_g, _) = _both(G, desc, dv)
+    (y_a, _), (y_g, b_g) = _both(G, desc, dv)
     assert torch.equal(y_a, y_g)
+    toks = sample_tokens(cfg.T, 48, 17, (0, cfg.T - 1))
+    check_tokens_vs_oracle(cfg, inp, y_g, host(b_g.topk_idx), toks, -1, "gathered y, Mixtral")
 
 
 @pytest.mark.parametrize("name,T", [("small_bf16", 1024), ("finegrained_bf16", 1024),
@@ -127,3 +135,11 @@ def test_ablation_baselines_give_the_grouped_bits(name, T):
     assert torch.equal(y_pe[lo:hi], y_grp[lo:hi])
     assert torch.equal(y_pad[lo:hi], y_grp[lo:hi])
     assert info["real_rows"] == int(hi - lo)
+    # each baseline's rows against the oracle's f_e of the token they hold
+    rows = np.unique(np.linspace(lo, hi - 1, 64).astype(int)) if hi > lo else np.zeros(0, int)
+    offs, src = host(b.offsets), host(b.src_token)
+    ri = torch.as_tensor(rows, device="cuda")
+    for tag, yy in (("per expert", y_pe), ("padded", y_pad)):
+        err = check_rows_vs_oracle(cfg, inp, host(yy[ri]), rows, src, offs,
+                                   f"ablation {tag} {name}")
+        say(f"  {tag}: oracle err on {len(rows)} rows {err}")

@@ -7,7 +7,8 @@ import torch
 
 from oracle import moe_oracle as O
 from tests.gpu_util import (LOGIT_TOL, TOL, assert_close, certified_route_mismatch, check_plan,
-                            dev, host, lib, run_layer, say, upload_layer)
+                            check_rows_vs_oracle, check_tokens_vs_oracle, dev, edge_rows, host,
+                            lib, run_layer, sample_tokens, say, upload_layer)
 from workloads import (CONFIGS, identity_scale_experts, make_inputs, marker_tokens,
                        small_layer_config)
 
@@ -114,26 +115,65 @@ def test_layer_shapes_reduced_tokens(name):
 def test_layer_full_size_sampled(name):
     """The layer at its full size, in the launch configuration the benchmark
     times: routing and plan are checked on every token, x_perm on sampled
-    rows, y on 64 sampled tokens against the per-token brute force."""
+    rows, and the oracle checks a stratified sample: y on 64 random tokens
+    plus every token whose row sits at an edge of an expert's row tiles (all
+    rows of each expert's last tile when it is short: the tiles the expert
+    GEMMs run on half their waves and move into their leftover launch, whose
+    weight loads are non-temporal when the experts' weights exceed the
+    last-level cache), and the expert outputs y_perm of those rows."""
     G = lib()
     cfg = CONFIGS[name]
     say(f"full {name}: drawing inputs")
     inp = make_inputs(cfg)
-    rng = np.random.default_rng(99)
-    sample = sorted(set(rng.choice(cfg.T, size=min(64, cfg.T), replace=False).tolist()) | {0, cfg.T - 1})
+    el = cfg.E // cfg.ep_size
     for cf in cfg.capacity_factors:
         cap = O.capacity_from_factor(cf, cfg.T, cfg.k, cfg.E)
         say(f"full {name} cf={cf}: running")
         desc, dv = upload_layer(G, cfg, inp, capacity=cap)
         y, bufs, _ = run_layer(G, desc, dv)
-        ref, near = _check_layer(G, cfg, inp, desc, y, bufs, cap, sample=sample)
+        ref, near = _check_layer(G, cfg, inp, desc, y, bufs, cap,
+                                 sample=sample_tokens(cfg.T, 64, 99, (0, cfg.T - 1)))
         assert len(near) <= max(2, cfg.T // 2000)
         counts = ref["counts"]
         say(f"  histogram (first 16 experts) {counts[:16].tolist()}, empty experts "
             f"{int((counts == 0).sum())}, dropped {int((ref['dest'] == -1).sum())}, "
             f"splits {ref['send_splits'].tolist()}")
+        rows = edge_rows(ref["offsets"], cfg.ep_rank * el, (cfg.ep_rank + 1) * el,
+                         desc.max_rows, short_all=128 if el <= 8 else 0,
+                         per_edge=4 if el > 8 else 8, seed=7)
+        src = ref["src_token"]
+        err = check_rows_vs_oracle(cfg, inp, host(bufs.y_perm[torch.as_tensor(rows, device="cuda")]),
+                                   rows, src, ref["offsets"], f"y_perm edge rows {name}")
+        toks = sorted(set(int(src[r]) for r in rows))
+        err2 = check_tokens_vs_oracle(cfg, inp, y, host(bufs.topk_idx), toks, cap,
+                                      f"y edge tokens {name}")
+        say(f"  edge rows {len(rows)} (tokens {len(toks)}): y_perm err {err}, y err {err2}")
         del dv, y, bufs
         torch.cuda.empty_cache()
+
+
+def test_optional_outputs_left_null():
+    """The fused call with every optional buffer NULL (the workspace holds
+    the routing and plan) gives y bitwise equal to the call with every
+    buffer given, in both dispatch modes, and within tolerance of the oracle."""
+    G = lib()
+    for name, T in (("finegrained_bf16", 1024), ("tiny_fp32", 64), ("ep_share_bf16", 256)):
+        base = CONFIGS[name]
+        cfg = small_layer_config(base, T)
+        inp = make_inputs(cfg)
+        cap = O.capacity_from_factor(base.capacity_factors[-1], cfg.T, cfg.k, cfg.E)
+        say(f"optional outputs NULL: {name} T={T} cap={cap}")
+        desc, dv = upload_layer(G, cfg, inp, capacity=cap)
+        y_full, b_full, ws = run_layer(G, desc, dv)
+        for gather in (False, True):
+            b = G.alloc_buffers(desc, x_perm=not gather, outputs=False)
+            y = torch.full_like(y_full, float("nan"))
+            G.layer_forward(desc, dv["h"], dv["w_router"], dv["bias"], dv["w1"], dv["w2"], y,
+                            b, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_full), (name, gather)
+        check_tokens_vs_oracle(cfg, inp, y, host(b_full.topk_idx), range(T), cap,
+                               f"y {name} optional outputs NULL")
 
 
 def test_run_twice_bitwise_identical():

@@ -1,13 +1,17 @@
 """GPU parity of the slot-ordered FFN output (moe_grouped_ffn_slots) and its
 combine (moe_combine_slots): every computed slot row must hold the bits of
-y_perm[dest] from the plain path, rows of other slots stay untouched, and
-the combined output must equal moe_unpermute_combine's bit for bit."""
+y_perm[dest] from the plain path, rows of other slots stay untouched, the
+combined output must equal moe_unpermute_combine's bit for bit, and both
+are checked against the oracle: slot rows against f_e of their token, the
+combined output against the per-token oracle (or the oracle layer when rows
+are clamped), each slot's expert output weighted by its own token's gate."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import moe_oracle as O
-from tests.gpu_util import host, lib, run_layer, say, upload_layer
+from tests.gpu_util import (TOL, assert_close, check_rows_vs_oracle, check_tokens_vs_oracle, host,
+                            lib, run_layer, sample_tokens, say, upload_layer)
 from workloads import CONFIGS, make_inputs, small_layer_config
 
 pytestmark = pytest.mark.gpu
@@ -41,6 +45,26 @@ def _check(desc, b, y, y_slots, y2, el):
     return int(used.sum())
 
 
+def _oracle(cfg, inp, b, y2, y_slots, cap, seed=0, n_tok=96, n_slots=64):
+    """y2 on sampled tokens against the per-token oracle; sampled slot rows
+    of y_slots against f_e of their token."""
+    T, k = cfg.T, cfg.k
+    gi = host(b.topk_idx)
+    toks = sample_tokens(T, n_tok, seed, (0, T - 1))
+    e1 = check_tokens_vs_oracle(cfg, inp, y2, gi, toks, cap, f"y from slots {cfg.name}")
+    el = cfg.E // cfg.ep_size
+    dest = host(b.dest).astype(np.int64)
+    used = (dest >= 0) & ((gi // el) == cfg.ep_rank)
+    t, j = np.nonzero(used)
+    if len(t) > n_slots:
+        pick = np.random.default_rng(seed).choice(len(t), n_slots, replace=False)
+        t, j = t[pick], j[pick]
+    e2 = check_rows_vs_oracle(cfg, inp, host(y_slots[torch.from_numpy(t * k + j).cuda()]),
+                              dest[t, j], host(b.src_token), host(b.offsets),
+                              f"slot rows {cfg.name}")
+    say(f"  oracle: y err {e1}, slot rows err {e2} ({len(toks)} tokens, {len(t)} slots)")
+
+
 # (layer, tokens, ep_size, ep_rank)
 CASES = [("tiny_fp32", 64, 1, 0), ("small_bf16", 1024, 1, 0), ("small_bf16", 1024, 4, 1),
          ("mixtral_bf16", 256, 1, 0), ("finegrained_bf16", 1024, 1, 0),
@@ -61,6 +85,7 @@ def test_slot_rows_and_combine_bit_identical(name, T, ep, rank):
         y_slots, y2 = _slots_path(G, desc, dv, b, ws)
         n = _check(desc, b, y, y_slots, y2, cfg.E // cfg.ep_size)
         say(f"  {n} slot rows checked")
+        _oracle(cfg, inp, b, y2, y_slots, cap, seed=T + ep)
 
 
 def test_slots_with_rows_clamped_to_max_rows():
@@ -72,6 +97,11 @@ def test_slots_with_rows_clamped_to_max_rows():
     assert int(host(b.flags)[0]) & G.FLAG_ROW_OVERFLOW
     y_slots, y2 = _slots_path(G, desc, dv, b, ws)
     _check(desc, b, y, y_slots, y2, cfg.E)
+    # slots past max_rows are not computed: the oracle layer with the same
+    # row limit, on the GPU's routing
+    ref = O.layer(inp["h"], inp["w_router"], inp["bias"], inp["w1"], inp["w2"], k=cfg.k,
+                  gate=cfg.gate, act=cfg.act, max_rows=900, route_idx=host(b.topk_idx))
+    assert_close(host(y2), ref["y"], TOL[cfg.dtype], "y from slots, rows clamped")
 
 
 @pytest.mark.slow
@@ -83,3 +113,4 @@ def test_slots_full_mixtral_layer():
     y, b, ws = run_layer(G, desc, dv)
     y_slots, y2 = _slots_path(G, desc, dv, b, ws)
     _check(desc, b, y, y_slots, y2, cfg.E)
+    _oracle(cfg, inp, b, y2, y_slots, -1, seed=3, n_tok=64, n_slots=64)
