@@ -30,6 +30,7 @@ FLAG_ROW_OVERFLOW, FLAG_BAD_EXPERT_ID, FLAG_NONFINITE_LOGIT, FLAG_DROPPED = 1, 2
 
 EXPORTED = ("moe_capacity_from_factor", "moe_workspace_size", "moe_route",
             "moe_topk_from_logits", "moe_permute", "moe_grouped_ffn",
+            "moe_permute_no_workspace",
             "moe_grouped_ffn_gather", "moe_grouped_ffn_slots", "moe_pack_dedup",
             "moe_unpermute_combine", "moe_combine_slots",
             "moe_layer_forward", "moe_status_str")
@@ -69,6 +70,7 @@ def _load():
         "moe_route": (I32, [D, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_topk_from_logits": (I32, [D, P, P, P, P, P]),
         "moe_permute": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "moe_permute_no_workspace": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, P]),
         "moe_grouped_ffn": (I32, [D, P, P, P, P, P, P, P, SZ, P]),
         "moe_grouped_ffn_gather": (I32, [D, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_pack_dedup": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
@@ -253,6 +255,26 @@ def permute(desc, h, topk_idx, x_perm, counts, offsets, dest, src_token, src_slo
         _ptr(send_splits, "send_splits", torch.int64, (desc.ep_size,)),
         _ptr(send_displs, "send_displs", torch.int64, (desc.ep_size,)),
         _ptr(flags, "flags", torch.int32, (1,)), wsp, wsn, _stream(stream)), "moe_permute")
+
+
+def permute_no_workspace(desc, h, topk_idx, x_perm, counts, offsets, dest, src_token,
+                         src_slot, send_splits, send_displs, flags, stream=None):
+    """permute without a workspace: the plan's scratch is the library's fixed
+    per-GPU array (calls that overlap on one GPU race)."""
+    dt = torch_dtype(desc)
+    T, d, E, k, R = desc.T, desc.d, desc.E, desc.k, desc.max_rows
+    _check(_lib.moe_permute_no_workspace(
+        ctypes.byref(desc), _ptr(h, "h", dt, (T, d)),
+        _ptr(topk_idx, "topk_idx", torch.int32, (T, k)),
+        _ptr(x_perm, "x_perm", dt, (R, d), optional=True),
+        _ptr(counts, "counts", torch.int32, (E,)),
+        _ptr(offsets, "offsets", torch.int32, (E + 1,)),
+        _ptr(dest, "dest", torch.int32, (T, k)),
+        _ptr(src_token, "src_token", torch.int32, (R,)),
+        _ptr(src_slot, "src_slot", torch.int32, (R,)),
+        _ptr(send_splits, "send_splits", torch.int64, (desc.ep_size,)),
+        _ptr(send_displs, "send_displs", torch.int64, (desc.ep_size,)),
+        _ptr(flags, "flags", torch.int32, (1,)), _stream(stream)), "moe_permute_no_workspace")
 
 
 def _w_shapes(desc):

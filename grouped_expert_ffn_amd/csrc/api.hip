@@ -2,6 +2,8 @@
 // enqueued on the caller's stream. Nothing here synchronises, copies device
 // data to the host or allocates memory.
 #include <algorithm>
+#include <atomic>
+
 #include "common.h"
 
 #define MOE_EXPORT extern "C" __attribute__((visibility("default")))
@@ -443,6 +445,58 @@ MOE_EXPORT moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const vo
   return do_combine(d, b->y_perm, idx, gate, dest, y, s);
 }
 
+// ---------------------------------------------------------------------------
+// moe_permute without a workspace, for callers that cannot allocate. Its only
+// scratch, the per-tile expert histograms of the plan, lives in this fixed
+// device array (one copy per GPU, held until the process ends). Host code
+// reaches it only through the device address hipGetSymbolAddress returns,
+// looked up once per device on the first call with that device current.
+constexpr int64_t kNoWsHistInts = int64_t(1) << 20;   // 4 MiB of int32 counts
+static __device__ __align__(256) int32_t scratch[kNoWsHistInts];
+
+static std::atomic<int32_t*> g_scratch_ptr[64];
+
+static moe_status_t no_ws_scratch(int32_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  int32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return MOE_ERR_HIP;
+    p = static_cast<int32_t*>(q);
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+MOE_EXPORT moe_status_t moe_permute_no_workspace(
+    const moe_layer_desc_t* desc, const void* h, const int32_t* topk_idx, void* x_perm,
+    int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src_token, int32_t* src_slot,
+    int64_t* send_splits, int64_t* send_displs, uint32_t* flags, void* stream) {
+  MOE_TRY(check_desc(desc));
+  const moe_layer_desc_t& d = *desc;
+  const int64_t Tk = d.T * d.k, R = d.max_rows;
+  MOE_TRY(check_bufs(desc, {{h, d.T * d.d, true}, {x_perm, x_perm ? R * d.d : 0, true},
+                            {topk_idx, Tk, false},
+                            {counts, d.E, false}, {offsets, d.E + 1, false}, {dest, Tk, false},
+                            {src_token, R, false}, {src_slot, R, false}, {flags, 1, false},
+                            {send_splits, d.ep_size, false}, {send_displs, d.ep_size, false}}));
+  const int64_t n_tiles = (d.T + kTokTile - 1) / kTokTile;
+  if (n_tiles * d.E > kNoWsHistInts) return MOE_ERR_SCRATCH;
+  int32_t* tile_hist = nullptr;
+  MOE_TRY(no_ws_scratch(&tile_hist));
+  hipStream_t s = (hipStream_t)stream;
+  // every histogram entry the plan reads is written first in the same call,
+  // so nothing left from an earlier call needs clearing
+  HIP_TRY(launch_dispatch_plan(topk_idx, tile_hist, counts, offsets, dest, src_token, src_slot,
+                               send_splits, send_displs, flags, d.T, d.E, d.k, d.capacity,
+                               d.max_rows, d.ep_size, s));
+  if (x_perm)
+    HIP_TRY(launch_permute_rows(h, dest, x_perm, d.T, d.k, (int)(d.d * elt_bytes(d.dtype)), s));
+  return MOE_OK;
+}
+
 MOE_EXPORT const char* moe_status_str(moe_status_t st) {
   switch (st) {
     case MOE_OK: return "ok";
@@ -453,6 +507,8 @@ MOE_EXPORT const char* moe_status_str(moe_status_t st) {
     case MOE_ERR_UNSUPPORTED: return "unknown gate or activation mode";
     case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MOE_ERR_HIP: return "a HIP kernel launch failed";
+    case MOE_ERR_SCRATCH:
+      return "the problem exceeds the fixed device scratch of the no-workspace entry point";
   }
   return "unknown status";
 }

@@ -53,7 +53,8 @@ typedef enum {
   MOE_ERR_DTYPE = 4,       /* unknown dtype */
   MOE_ERR_UNSUPPORTED = 5, /* unknown gate or activation mode */
   MOE_ERR_WORKSPACE = 6,   /* workspace missing, misaligned or too small */
-  MOE_ERR_HIP = 7          /* a kernel launch failed */
+  MOE_ERR_HIP = 7,         /* a kernel launch failed */
+  MOE_ERR_SCRATCH = 8      /* beyond the fixed scratch of moe_permute_no_workspace */
 } moe_status_t;
 
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
@@ -158,6 +159,25 @@ moe_status_t moe_permute(const moe_layer_desc_t* desc, const void* h, const int3
                          int32_t* src_token, int32_t* src_slot, int64_t* send_splits,
                          int64_t* send_displs, uint32_t* flags, void* ws, size_t ws_bytes,
                          void* stream);
+
+/* moe_permute for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments and results as moe_permute, without the workspace.
+ * The plan's per-tile expert histograms go to a fixed 4 MiB device array
+ * inside the library instead, one per GPU, allocated when the library is
+ * loaded and held until the process ends; the call itself allocates
+ * nothing. Limit: ceil(T / 128) * E <= 2^20 (for example T <= 131072 tokens
+ * at E = 1024), else MOE_ERR_SCRATCH before anything is enqueued. Every
+ * call on one GPU shares that array: calls that overlap on a GPU (other
+ * streams, other threads) race and must be ordered by the caller. Nothing
+ * in the array needs clearing between calls (each call writes every entry it
+ * reads). The first call on a device, with that device current, looks up the
+ * array's device address (a HIP runtime query, no allocation). */
+moe_status_t moe_permute_no_workspace(const moe_layer_desc_t* desc, const void* h,
+                                      const int32_t* topk_idx, void* x_perm, int32_t* counts,
+                                      int32_t* offsets, int32_t* dest, int32_t* src_token,
+                                      int32_t* src_slot, int64_t* send_splits,
+                                      int64_t* send_displs, uint32_t* flags, void* stream);
 
 /* Grouped expert FFN: for every local expert e, rows offsets[e]..offsets[e+1]-1
  * (clamped to max_rows) of x_perm go through f_e into the same rows of y_perm

@@ -58,7 +58,7 @@ def test_workspace_size_grows_with_rows(G):
 
 
 def test_status_strings(G):
-    for s in range(8):
+    for s in range(9):
         assert G.status_str(s)
     assert G.status_str(0) == "ok"
 
@@ -186,3 +186,19 @@ def test_product_code_never_reaches_the_oracle():
     assert files
     for p in files:
         assert not re.search(r"\boracle\b|moe_oracle", open(p).read()), p
+
+
+def test_permute_no_workspace_limit(G):
+    """The no-workspace permute holds its plan histograms in a fixed 2^20-entry
+    device array: ceil(T / 128) * E above that is refused with
+    MOE_ERR_SCRATCH before anything is enqueued; other argument errors are
+    the ones moe_permute reports."""
+    p = ctypes.c_void_p
+    args = [p(1 << 20)] * 11
+    big = G.make_desc(131073, 64, 1024, 2, 64, "bf16", "softmax", "swiglu")   # 1025 tiles
+    assert G._lib.moe_permute_no_workspace(ctypes.byref(big), *args, None) == 8
+    assert "fixed device scratch" in G.status_str(8)
+    assert G._lib.moe_permute_no_workspace(None, *args, None) == 1
+    ok = G.make_desc(131072, 64, 1024, 2, 64, "bf16", "softmax", "swiglu")
+    args[1] = p(2)            # misaligned topk_idx
+    assert G._lib.moe_permute_no_workspace(ctypes.byref(ok), *args, None) == 3
