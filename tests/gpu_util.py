@@ -131,13 +131,13 @@ def edge_rows(offsets, e_lo, e_hi, max_rows, bm=256, short_all=128, per_edge=8, 
     short tile, the kind the GEMMs run on half their waves and move into the
     leftover launch; else `per_edge` from each end and a few inside)."""
     rng = np.random.default_rng(seed)
-    rows = set()
     offs = np.asarray(offsets, np.int64)
+    out = []
     for e in range(e_lo, e_hi):
         r0, r1 = min(int(offs[e]), max_rows), min(int(offs[e + 1]), max_rows)
         if r1 <= r0:
             continue
-        rows.update(range(r0, min(r1, r0 + per_edge)))
+        rows = set(range(r0, r0 + per_edge))
         mt = (r1 - r0 + bm - 1) // bm
         t0 = r0 + (mt - 1) * bm
         if r1 - t0 <= short_all:
@@ -146,7 +146,9 @@ def edge_rows(offsets, e_lo, e_hi, max_rows, bm=256, short_all=128, per_edge=8, 
             rows.update(range(t0, t0 + per_edge))
             rows.update(range(r1 - per_edge, r1))
             rows.update(rng.integers(t0, r1, per_edge).tolist())
-    return sorted(rows)
+        # only this expert's own rows: [r0, r1), all below max_rows
+        out.extend(r for r in rows if r0 <= r < r1)
+    return sorted(set(out))
 
 
 def check_tokens_vs_oracle(cfg, inp, y, idx_gpu, toks, capacity=-1, what="y", T=None):
