@@ -75,15 +75,32 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void router_skinny_kernel(
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nks = d / 32;
-#pragma unroll 4
-  for (int ks = wave; ks < nks; ks += kSkinnyWaves) {
-    const bf16x8 hv = *reinterpret_cast<const bf16x8*>(hp + ks * 32);
+  // this wave's K steps are wave, wave + 8, ...; the loads of U of them are
+  // issued before their MFMAs, so U token-row loads per wave are in flight
+  // (the token rows stream once: non-temporal, leaving W_r^T in the cache)
+  constexpr int U = 8;
+  for (int ks0 = wave; ks0 < nks; ks0 += U * kSkinnyWaves) {
+    bf16x8 hv[U], wv[U][NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      // rows E..E_pad-1 of W_r^T are zero: their lanes skip the load
-      bf16x8 wv = {};
-      if (b * 16 + lr < E) wv = *reinterpret_cast<const bf16x8*>(wp + (int64_t)b * 16 * d + ks * 32);
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, hv, acc[b], 0, 0, 0);
+    for (int u = 0; u < U; ++u) {
+      const int ks = ks0 + u * kSkinnyWaves;
+      hv[u] = bf16x8{};
+      if (ks < nks) hv[u] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(hp + ks * 32));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        // rows E..E_pad-1 of W_r^T are zero: their lanes skip the load
+        wv[u][b] = bf16x8{};
+        if (ks < nks && b * 16 + lr < E)
+          wv[u][b] = *reinterpret_cast<const bf16x8*>(wp + (int64_t)b * 16 * d + ks * 32);
+      }
+    }
+    // MFMAs in ascending K, as one chain per output
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ks0 + u * kSkinnyWaves >= nks) break;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[u][b], hv[u], acc[b], 0, 0, 0);
     }
   }
 #pragma unroll

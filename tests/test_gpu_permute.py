@@ -172,3 +172,19 @@ def test_large_plan_takes_the_separate_scan_path(cap):
     desc, bufs, h = _permute(G, idx, E, capacity=cap, d=64)
     ref = check_plan(G, desc, idx, bufs, E, cap, T * k)
     _check_rows(bufs, h, ref)
+
+
+@pytest.mark.parametrize("T,E,k", [(8192, 8, 2), (8193, 8, 2), (16000, 16, 2), (4096, 1024, 4),
+                                   (2048, 256, 8), (2049, 256, 8)])
+def test_plan_paths_around_the_size_switches(T, E, k):
+    """Plans with at most 4096 tile x expert counts are scanned inside the
+    rank launch, larger ones by a separate scan launch; cases around that
+    switch and at the layer sizes (2^14 assignments), with and without
+    capacity, must match the oracle."""
+    G = lib()
+    rng = np.random.default_rng(T + E)
+    idx = _skewed_routes(rng, T, E, k)
+    for cap in (-1, max(1, T * k // E - 3)):
+        desc, bufs, h = _permute(G, idx, E, capacity=cap, d=64)
+        ref = check_plan(G, desc, idx, bufs, E, cap, T * k)
+        _check_rows(bufs, h, ref)
