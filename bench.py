@@ -87,6 +87,21 @@ def measured_traffic(workload):
     return float(m_b.group(1))
 
 
+def measured_clock(workload):
+    """Time-weighted shader clock (GHz) of the expert GEMM kernels from the
+    committed rocprofv3 counter summary (GRBM_GUI_ACTIVE per dispatch), if it
+    was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"mfma_grouped_ffn_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"^source_sha:\s*(\w+)", text, re.M)
+    m_c = re.search(r"^gemm_clock_ghz:\s*([0-9.]+)", text, re.M)
+    if not m_sha or not m_c or m_sha.group(1) != kernel_source_sha():
+        return None
+    return float(m_c.group(1))
+
+
 def host_description():
     """CPU model and the BLAS numpy links, for the CPU baseline's record."""
     model = None
@@ -179,11 +194,14 @@ def gpu_clock_during(run, n_steps):
                 if int(bdf.split(":")[1], 16) == int(bus):
                     handle = h
                     break
+        acc = []
+
         def read():
-            # the SMU's metrics table (refreshed about every millisecond) has
-            # the current GFX clock of every XCD; the clock-info query's value
-            # can lag behind it
+            # the SMU's metrics table (refreshed about every millisecond where
+            # the host allows it) has the current GFX clock of every XCD; its
+            # activity accumulator shows whether the table was refreshed
             m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+            acc.append(m.get("gfx_activity_acc"))
             per_xcd = [v for v in (m.get("current_gfxclks") or [])
                        if isinstance(v, (int, float)) and 0 < v < 65535]
             cur = m.get("current_gfxclk")
@@ -217,9 +235,13 @@ def gpu_clock_during(run, n_steps):
         pass
     if not samples and not avgs:
         return {"error": "no clock sample while the steps ran"}
+    refreshed = len(set(a for a in acc if a is not None)) > 1
     rec = {"samples": len(samples), "steps": n_steps, "span_s": span, "max_clk_mhz": max_clk,
+           "metrics_refreshed": refreshed,
            "source": "amdsmi GPU metrics (current GFX clock averaged over the XCDs, and the "
-                     "SMU's own running average), sampled while the steps ran"}
+                     "SMU's own running average), sampled while the steps ran"
+                     + ("" if refreshed else "; the table did not change while the steps ran, "
+                        "so these values do not describe them")}
     if samples:
         rec.update(gfx_mhz_median=float(np.median(samples)), gfx_mhz_min=min(samples),
                    gfx_mhz_max=max(samples))
@@ -625,7 +647,10 @@ def main():
                    "step_ms_min": float(step_ms.min()), "step_ms_max": float(step_ms.max()),
                    "wall_s_incl_evictions": wall},
         "warm_mall": warm,
-        "gpu_clock": clock,
+        "gpu_clock": dict(clock or {}, gemm_clock_ghz_counters=measured_clock(cfg.name),
+                          gemm_clock_source="GRBM_GUI_ACTIVE / 8 XCDs / duration of the expert "
+                          "GEMM dispatches, time-weighted, from the committed rocprofv3 summary "
+                          "of this workload on the same kernel sources (null otherwise)"),
         "env": env_record(torch),
     }
     if args.ablation:
