@@ -34,13 +34,18 @@ int device_cu_count();
 // moved tiles reach into it. Short tiles elsewhere keep their place beside
 // their expert's full tiles (a layer without leftover tiles keeps the plain
 // expert order).
+//
+// ride: an expert's short last tile of s rows instead rides on its full
+// tiles, 16 rows on each of ceil(s / 16) of them per column tile (entry
+// fields x and w; set_rider picks the tiles), when it has that many full
+// tiles (and fewer than 2^14); it then needs no weight pass of its own.
 __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restrict__ offsets,
                                                         int e_lo, int E_loc, int64_t max_rows,
                                                         int BM, int4* __restrict__ tiles1,
                                                         int4* __restrict__ tiles2,
                                                         int* __restrict__ n_tiles_out, int n_n1,
                                                         int G1, int n_n2, int G2, int group_m,
-                                                        uint32_t* __restrict__ flags) {
+                                                        uint32_t* __restrict__ flags, int ride) {
   // one thread per local expert (64 per wave); scans within a wave by
   // shuffles, across waves through LDS
   __shared__ int wsum_m[16], wsum_s[16], wmax[2][16];
@@ -50,11 +55,21 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
   if (tid == 0 && flags && (int64_t)offsets[e_lo + E_loc] > max_rows)
     atomicOr(flags, MOE_FLAG_ROW_OVERFLOW);
   int r0 = 0, r1 = 0, mt = 0, sh = 0;
+  int rb = 0, r_first = 0;   // rider row blocks, first rider row
   if (tid < E_loc) {
     r0 = (int)min((int64_t)offsets[e_lo + tid], max_rows);
     r1 = (int)min((int64_t)offsets[e_lo + tid + 1], max_rows);
     mt = r1 > r0 ? (r1 - r0 + BM - 1) / BM : 0;
     sh = (mt > 0 && r1 - r0 - (mt - 1) * BM <= BM / 2) ? 1 : 0;
+    if (ride && sh && mt >= 2 && mt <= (1 << 14) - 1) {
+      const int need = (r1 - r0 - (mt - 1) * BM + 15) / 16;
+      if (need <= mt - 1) {
+        rb = need;
+        mt -= 1;
+        sh = 0;
+        r_first = r0 + mt * BM;
+      }
+    }
   }
   int im = mt, is = sh;   // inclusive scans within the wave
 #pragma unroll
@@ -99,7 +114,10 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
     const int start = im - mt - moved_before;
     for (int m = 0; m < mt - mv; ++m) {
       const int a = r0 + m * BM;
-      tab[start + m] = make_int4(tid, a, min(a + BM, r1), 0);
+      if (rb)
+        tab[start + m] = make_int4(tid | ((r1 - r_first) << 10) | (mt << 18), a, a + BM, r_first);
+      else
+        tab[start + m] = make_int4(tid, a, min(a + BM, r1), 0);
     }
     int rows_mv = 0;
     if (mv) {
@@ -126,10 +144,41 @@ __global__ __launch_bounds__(1024) void tile_map_kernel(const int32_t* __restric
 // loops look it up right after a slice barrier or after an epilogue, where
 // no LDS read is outstanding, so waiting for the scalar load costs only its
 // own latency; a vector load would also wait for every slice load in flight.
+// Entry fields: x = local expert | s << 10 | m << 18, y = first row, z = end
+// row, w = first row past the expert's full tiles. s > 0: the expert's last
+// s rows (s <= 128) ride on its m full tiles (see tile_map_kernel).
 __device__ __forceinline__ int4 tile_entry(const int4* __restrict__ tiles, int mt) {
   using CInt = const __attribute__((address_space(4))) int;
   CInt* p = (CInt*)tiles + 4 * mt;
-  return make_int4(p[0], p[1], p[2], 0);
+  return make_int4(p[0], p[1], p[2], p[3]);
+}
+
+__device__ __forceinline__ int entry_expert(const int4& e) { return e.x & 0x3ff; }
+
+// The rider of full tile e in column tile nt, for A (gathered: rows) with row
+// stride K: the expert's s remainder rows form rb = ceil(s / 16) blocks of 16,
+// and in column tile nt block i rides on the expert's full tile
+// (i + rb * (nt + nt / S)) mod m. A workgroup of the persistent walk keeps
+// its place in the M-tile group from round to round while its column tile
+// moves on by S (the grid's column tiles per round), so the nt / S term
+// shifts the rb riding tiles by rb places from round to round, and no
+// workgroup carries a rider in every round.
+template <bool GA, int BM>
+__device__ __forceinline__ void set_rider(GemmTile& t, const int4& e, int nt, int S,
+                                          const bf16* A, const int32_t* rows, int K) {
+  t.r_rows = 0;
+  const int s = (e.x >> 10) & 0xff;
+  if (s == 0) return;
+  const int m = (int)((uint32_t)e.x >> 18);
+  const int rb = (s + 15) / 16;
+  const int ml = m - (e.w - e.y) / BM;    // this tile's index among the m
+  int i = (ml - rb * (nt % m + nt / S % m) % m) % m;
+  if (i < 0) i += m;
+  if (i >= rb) return;
+  t.r_rows = min(16, s - 16 * i);
+  t.r_crow = e.w + 16 * i;
+  t.ra = GA ? A : A + t.r_crow * K;
+  t.rrows = GA ? rows + t.r_crow : nullptr;
 }
 
 // Tiles that do not fill a whole round of the persistent grid: when they
@@ -149,13 +198,14 @@ __device__ __forceinline__ int main_tile_end(int total, int G) {
 // GA (gathered A): A row i of the grouped operand is row rows[i] of A, so the
 // token rows need not be copied into expert order first (the fused layer
 // call's dispatch); otherwise A is the expert-ordered matrix itself.
-template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA>
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA,
+          bool RIDE>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ rows, const bf16* __restrict__ W,
     bf16* __restrict__ C, const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr,
     int N, int K, int64_t w_stride, int n_n, int64_t ldc, const int32_t* __restrict__ o_tok,
     const int32_t* __restrict__ o_slot, int o_k) {
-  using TG = TileGemmDL<BM, BN, WM, WN, EPI, BK, MF, GA>;
+  using TG = TileGemmDL<BM, BN, WM, WN, EPI, BK, MF, GA, 2, RIDE>;
   __shared__ __attribute__((aligned(1024))) bf16 lds[TG::LDS_ELEMS];
   const int n_m = *n_mt_ptr;
   const int G = gridDim.x;
@@ -167,8 +217,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
     if (v >= end) return false;
     int mt, nt;
     tile_coords<GROUP_M>(v, n_m, n_n, mt, nt);
-    const int4 e = tile_entry(tiles, mt);   // expert, first row, end row
-    const int ex = e.x, ey = e.y, ez = e.z;
+    const int4 e = tile_entry(tiles, mt);
+    const int ex = entry_expert(e), ey = e.y, ez = e.z;
     t.a = GA ? A : A + (int64_t)ey * K;
     t.rows = GA ? rows + ey : nullptr;
     t.a_rows = ez - ey;
@@ -179,6 +229,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
     t.o_tok = o_tok;
     t.o_slot = o_slot;
     t.o_k = o_k;
+    if constexpr (RIDE) set_rider<GA, BM>(t, e, nt, max(1, G / GROUP_M), A, rows, K);
     return true;
   };
   TG::run_tiles(get, N, K, C, ldc, lds);
@@ -191,12 +242,13 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
 // loop waits on memory rather than on the MFMAs: it keeps as many slice
 // buffers (up to five, four slices in flight) as fit in the 160 KiB of LDS.
 template <int SM, int SN, int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF,
-          bool GA>
+          bool GA, bool RIDE>
 struct TailPieces {
   static constexpr int HM = BM / SM, HN = BN / SN, S = SM * SN;
-  static constexpr int BUF_BYTES = TileGemmDL<HM, HN, WM, WN, EPI, BK, MF, GA, 2>::LDS_BUF * 2;
+  static constexpr int BUF_BYTES =
+      TileGemmDL<HM, HN, WM, WN, EPI, BK, MF, GA, 2, RIDE>::LDS_BUF * 2;
   static constexpr int NB = 160 * 1024 / BUF_BYTES;
-  using TG = TileGemmDL<HM, HN, WM, WN, EPI, BK, MF, GA, NB >= 5 ? 5 : NB < 2 ? 2 : NB>;
+  using TG = TileGemmDL<HM, HN, WM, WN, EPI, BK, MF, GA, NB >= 5 ? 5 : NB < 2 ? 2 : NB, RIDE>;
   __device__ __forceinline__ static void run(const bf16* A, const int32_t* rows, const bf16* W,
                                              bf16* C, const int4* tiles, int n_m, int first,
                                              int left, int N, int K, int64_t w_stride, int n_n,
@@ -213,7 +265,7 @@ struct TailPieces {
         tile_coords<GROUP_M>(first + u / S, n_m, n_n, mt, nt);
         const int part = u % S;
         const int4 e = tile_entry(tiles, mt);
-        const int ex = e.x, ey = e.y + (part % SM) * HM, ez = e.z;
+        const int ex = entry_expert(e), ey = e.y + (part % SM) * HM, ez = e.z;
         if (ey >= ez) continue;
         const int n0 = nt * BN + (part / SM) * HN;
         if (n0 >= N) continue;
@@ -227,6 +279,13 @@ struct TailPieces {
         t.o_tok = o_tok;
         t.o_slot = o_slot;
         t.o_k = o_k;
+        // a tile's rider goes with its first row piece of each column piece
+        if constexpr (RIDE) {
+          if (part % SM == 0)
+            set_rider<GA, BM>(t, e, nt, max(1, (int)gridDim.x / GROUP_M), A, rows, K);
+          else
+            t.r_rows = 0;
+        }
         return true;
       }
       return false;
@@ -268,14 +327,14 @@ struct TailShort {
         for (int u = slot + i * (int)gridDim.x; u < units; u += gridDim.x) {
           int mt, nt;
           tile_coords<GROUP_M>(first + u / SN, n_m, n_n, mt, nt);
-          const int4 e = tile_entry(tiles, mt);
+          const int4 e = tile_entry(tiles, mt);   // a short tile: no rider
           const int n0 = nt * BN + (u % SN) * HN;
           if (n0 >= N) continue;
           t.a = GA ? A : A + (int64_t)e.y * K;
           t.rows = GA ? rows + e.y : nullptr;
           t.a_rows = min(e.z - e.y, HMQ);
           t.n0 = n0;
-          t.b = W + (int64_t)e.x * w_stride + (int64_t)n0 * K;
+          t.b = W + (int64_t)entry_expert(e) * w_stride + (int64_t)n0 * K;
           t.c_row = e.y;
           t.nk = nk;
           t.o_tok = o_tok;
@@ -294,16 +353,17 @@ struct TailShort {
 // The leftover tiles with the finest split S in {2, 4, 8} for which
 // S * leftover <= G (G: the main kernel's grid size, also this grid's).
 // Splitting by rows and columns leaves every output's K order unchanged.
-template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA>
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA,
+          bool RIDE>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_tail_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ rows, const bf16* __restrict__ W,
     bf16* __restrict__ C, const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr,
     int N, int K, int64_t w_stride, int n_n, int64_t ldc, const int32_t* __restrict__ o_tok,
     const int32_t* __restrict__ o_slot, int o_k, int G, const int* __restrict__ short_rows,
     int nt_w) {
-  using P2 = TailPieces<2, 1, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
-  using P4 = TailPieces<2, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
-  using P8 = TailPieces<4, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
+  using P2 = TailPieces<2, 1, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA, RIDE>;
+  using P4 = TailPieces<2, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA, RIDE>;
+  using P8 = TailPieces<4, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA, RIDE>;
   // all-short leftovers: 64- or 128-row pieces, column quarters, halves or whole
   using Q4 = TailShort<BM / 4, 4, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
   using Q2 = TailShort<BM / 4, 2, BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>;
@@ -393,7 +453,8 @@ static int gemm_grid(int64_t max_mtiles, int n_n, int per_cu) {
   return (int)max((int64_t)8, G / 8 * 8);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA = false>
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int GROUP_M, int MF, bool GA = false,
+          bool RIDE = true>
 static hipError_t grouped_gemm_dl_launch(const bf16* A, const int32_t* rows, const bf16* W,
                                          bf16* C, const int4* tiles, const int* n_mt, int N,
                                          int K, int64_t w_stride, int64_t ldc,
@@ -403,12 +464,12 @@ static hipError_t grouped_gemm_dl_launch(const bf16* A, const int32_t* rows, con
                                          const int32_t* o_slot = nullptr, int o_k = 0) {
   const int n_n = (N + BN - 1) / BN;
   const int G = gemm_grid(max_mtiles, n_n, per_cu);
-  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>),
+  hipLaunchKernelGGL((grouped_gemm_dl_kernel<BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA, RIDE>),
                      dim3((unsigned)G), dim3(64 * WM * WN), 0, s, A, rows, W, C, tiles, n_mt, N,
                      K, w_stride, n_n, ldc, o_tok, o_slot, o_k);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((grouped_gemm_tail_kernel<BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA>),
+  hipLaunchKernelGGL((grouped_gemm_tail_kernel<BM, BN, WM, WN, EPI, BK, GROUP_M, MF, GA, RIDE>),
                      dim3((unsigned)G), dim3(64 * WM * WN), 0, s, A, rows, W, C, tiles, n_mt, N,
                      K, w_stride, n_n, ldc, o_tok, o_slot, o_k, (int)G, short_rows, (int)nt_w);
   return hipGetLastError();
@@ -545,7 +606,7 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
     hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(tile_map_threads(el)), 0, s, offsets,
                        e_lo, el, desc.max_rows, kGemmBM, tiles, tiles2, n_mt, n_n1,
                        gemm_grid(mt_ub, n_n1, 1), n_n2, gemm_grid(mt_ub, n_n2, 1), kGemmGroupM,
-                       flags);
+                       flags, 1);
     const bf16* X = (const bf16*)x_perm;
     const bf16* W1 = (const bf16*)w1;
     bf16* H = (bf16*)act;
@@ -581,7 +642,7 @@ hipError_t launch_grouped_ffn(const moe_layer_desc_t& desc, const void* x_perm,
         H, nullptr, W2, Y, tiles2, n_mt, d, dff, s2, d, mt_ub, 1, s, n_mt + 2, nt_w);
   }
   hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(tile_map_threads(el)), 0, s, offsets, e_lo,
-                     el, desc.max_rows, kF32BM, tiles, tiles2, n_mt, 0, 0, 0, 0, 1, flags);
+                     el, desc.max_rows, kF32BM, tiles, tiles2, n_mt, 0, 0, 0, 0, 1, flags, 0);
   const float* X = (const float*)x_perm;
   float* H = (float*)act;
   if (swiglu)

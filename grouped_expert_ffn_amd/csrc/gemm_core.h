@@ -92,6 +92,15 @@ struct GemmTile {
   // weight slices loaded non-temporal (no reuse expected in the last-level
   // cache), so that they do not evict data a later kernel reads
   bool nt_w = false;
+  // rider: up to 16 more rows of the same expert (the short remainder of its
+  // group), multiplied with this tile's weight slices and stored beside its
+  // rows; r_rows = 0: none. ra: rider row 0 (row stride K), or with gathered
+  // rows the matrix base, rrows then holding the rider's row indices; r_crow:
+  // output row of rider row 0
+  int r_rows = 0;
+  const bf16* ra = nullptr;
+  const int32_t* rrows = nullptr;
+  int64_t r_crow = 0;
 };
 
 // Persistent tile loop of one workgroup: run_tiles(get, ...) multiplies the
@@ -104,8 +113,16 @@ struct GemmTile {
 // (a_rows <= BM / 2 with two wave rows) leaves the upper waves idle: they
 // still fetch their share of each slice and meet every barrier, but issue no
 // MFMAs, so the lower waves have their SIMDs to themselves.
+//
+// RIDE: a tile may carry a rider (GemmTile::r_rows), 16 rows of the same
+// expert that would otherwise form a short tile of their own, which would
+// stream the whole weight block again for a few rows. The rider's rows come
+// into a 16-row area after each slice (one extra load per wave, 16 lanes),
+// and every wave multiplies them with its own weight fragments for half of
+// its column tiles (the two wave rows take one half each): the same MFMAs,
+// operands and K order as in a tile of their own, so the same bits.
 template <int BM, int BN, int WM, int WN, int EPI, int BK = 64, int MF = 16, bool GA = false,
-          int NBUF = 2>
+          int NBUF = 2, bool RIDE = false>
 struct TileGemmDL {
   using L = SliceLayout<BK>;
   static constexpr int NT = 64 * WM * WN;
@@ -117,8 +134,11 @@ struct TileGemmDL {
   static constexpr int LPW = LOADS / NW;           // loads per wave per slice
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int TM = WTM / MF, TN = WTN / MF;   // MFMA tiles per wave
-  static constexpr int LDS_BUF = ROWS * BK;
+  static constexpr int RR = RIDE ? 16 : 0;          // rider rows per slice
+  static constexpr int LDS_BUF = (ROWS + RR) * BK;
   static constexpr int LDS_ELEMS = NBUF * LDS_BUF;
+  static constexpr int LPWR = LPW + (RIDE ? 1 : 0);  // loads per wave per slice
+  static constexpr int RX = TN >= 2 ? TN / 2 : 1;    // rider column tiles per wave
   using Acc = typename std::conditional<MF == 32, f32x16, f32x4>::type;
   static constexpr int NACC = MF == 32 ? 16 : 4;
   static constexpr int KSUB = MF == 32 ? 16 : 32;  // K per MFMA
@@ -127,7 +147,11 @@ struct TileGemmDL {
   static constexpr int TU = GATED ? TN : 1;
   static_assert(MF == 16 || MF == 32, "MFMA shape");
   static_assert(NBUF >= 2 && NBUF <= 5, "two to five slice buffers");
-  static_assert((NBUF - 2) * LPW < 64, "slices in flight must fit the vmcnt field");
+  static_assert((NBUF - 2) * LPWR < 64, "slices in flight must fit the vmcnt field");
+  // a rider: 16-row MFMA tiles, two rider rows per wave, two wave rows
+  static_assert(!RIDE || (MF == 16 && BK == 64 && WM == 2 && 2 * NW == RR &&
+                          EPI != EPI_ROUTER_F32),
+                "rider layout");
   static_assert(LOADS % NW == 0, "loads must split evenly over waves");
   static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be a multiple of the MFMA tile");
   static_assert(BK % 32 == 0 && NSUB >= 2, "two or more MFMA sub-steps per K slice");
@@ -160,6 +184,9 @@ struct TileGemmDL {
     // the row index itself, made a byte offset when the slice is fetched (so
     // the row-index load has a whole slice of MFMAs to arrive)
     uint32_t off[LPW];
+    // rider load: byte offset from the tile's ra (gathered rows: the row
+    // index, and the chunk's byte offset in rchunk)
+    uint32_t roff = 0, rchunk = 0;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) is_a[i] = (wave * LPW + i) * L::RPL < BM;
     // gathered A rows: byte offset of this lane's 16-byte chunk, for loads of
@@ -191,6 +218,20 @@ struct TileGemmDL {
           row = (GATED && q >= BN) ? N + nn : nn;
         }
         off[i] = ((uint32_t)row * (uint32_t)K + (uint32_t)(c * 8)) * 2u;
+      }
+      if constexpr (RIDE) {
+        // rider row rr (two per wave; lanes 2 * CPR and up load nothing),
+        // clamped onto the last rider row; a tile without a rider points
+        // its unused rider load at its own first row
+        const int rr = wave * 2 + (ln / L::CPR) % 2;
+        const int c = L::swz(rr, ln % L::CPR);
+        const int src = t.r_rows > 0 ? (rr < t.r_rows ? rr : t.r_rows - 1) : 0;
+        if constexpr (GA) {
+          roff = (uint32_t)(t.r_rows > 0 ? t.rrows[src] : t.rows[0]);
+          rchunk = (uint32_t)(c * 16);
+        } else {
+          roff = ((uint32_t)src * (uint32_t)K + (uint32_t)(c * 8)) * 2u;
+        }
       }
     };
     // When a wave's loads are all token rows or all weight rows (RPL * LPW
@@ -259,9 +300,28 @@ struct TileGemmDL {
     // the buffer the next slice goes to; slices issued so far (the slices of
     // all tiles form one sequence)
     int l_buf = 0, l_issued = 0;
+    // the rider's two rows of this wave for slice kt (16 lanes, 256 bytes,
+    // after the slice's A and weight rows in the buffer). With two buffers
+    // every slice wait is a full drain, so only tiles with a rider issue it;
+    // with more buffers the waits count loads, so every slice of every tile
+    // issues it and each wave's load count per slice stays fixed
+    auto issue_rider = [&](const GemmTile& t, int kt, int buf) {
+      if constexpr (RIDE) {
+        if (NBUF == 2 && t.r_rows == 0) return;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16*>(t.r_rows > 0 ? t.ra : t.a), (short)0, -1, 0x00020000);
+        const uint32_t o = GA ? roff * (uint32_t)(K * 2) + rchunk : roff;
+        bf16* base = lds + buf * LDS_BUF + ROWS * BK + wave * 2 * BK;
+        if (lane < 2 * L::CPR)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)base, 16, o, (uint32_t)kt * (BK * 2), 0,
+              0);
+      }
+    };
     auto issue_next = [&]() {
       if (!l_live) return;
       issue(lt, l_k, l_buf);
+      issue_rider(lt, l_k, l_buf);
       ++l_issued;
       l_buf = l_buf + 1 == NBUF ? 0 : l_buf + 1;
       if (++l_k == lt.nk) {
@@ -294,6 +354,23 @@ struct TileGemmDL {
             for (int q = 0; q < NACC; ++q) acc2[x][y][q] = 0.f;
       }
     };
+    // rider accumulators: half of this wave's column tiles, the lower half on
+    // the lower wave row and the upper half on the upper one (each SIMD runs
+    // one wave of each row, so each takes the same extra work); with a single
+    // column tile only the lower wave row has a rider part
+    Acc accr[RX];
+    Acc accr2[GATED ? RX : 1];
+    const bool r_wave = TN >= 2 || wm == 0;
+    const int xb = TN >= 2 ? wm * RX : 0;
+    auto zero_acc_r = [&]() {
+#pragma unroll
+      for (int x = 0; x < RX; ++x)
+#pragma unroll
+        for (int q = 0; q < NACC; ++q) {
+          accr[x][q] = 0.f;
+          if (GATED) accr2[GATED ? x : 0][q] = 0.f;
+        }
+    };
     const int lr = lane % MF;
     const int lq = lane / MF;
     auto mma = [&](const bf16x8& w, const bf16x8& x, Acc& c) {
@@ -310,6 +387,12 @@ struct TileGemmDL {
       bf16x8 w[TN], u[TU];
     };
     bf16x8 fy[TM];
+    bf16x8 fr;   // the rider's token-row fragment
+    auto read_r = [&](int buf, int ks) -> bf16x8 {
+      const bf16* Rs = lds + buf * LDS_BUF + ROWS * BK;
+      const int ci = ks * CPS + lq;
+      return *reinterpret_cast<const bf16x8*>(Rs + lr * BK + L::swz(lr, ci) * 8);
+    };
     auto read_a = [&](int buf, int ks, int y) -> bf16x8 {
       const bf16* As = lds + buf * LDS_BUF;
       const int ci = ks * CPS + lq;
@@ -330,7 +413,9 @@ struct TileGemmDL {
       }
     };
     // multiply one sub-step (token fragments fy, weight fragments cur); with
-    // RD, read sub-step nks of buffer nbuf into fy and nxt meanwhile
+    // RD, read sub-step nks of buffer nbuf into fy and nxt meanwhile; a
+    // tile's rider MFMAs (and rider fragment read) follow
+    bool has_r = false;   // the tile being multiplied carries a rider (uniform)
     auto step = [&](auto rd, const FragsB& cur, FragsB& nxt, int nbuf, int nks) {
       constexpr bool RD = decltype(rd)::value;
       if (RD) read_b(nbuf, nks, nxt);
@@ -359,6 +444,26 @@ struct TileGemmDL {
         for (int y = 1; y < TM; ++y) {
           __builtin_amdgcn_sched_group_barrier(0x008, MPY, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+      if constexpr (RIDE) {
+        // the rider's MFMAs and fragment read come after the sub-step's own,
+        // fenced off so that they leave its issue order alone; the wave row's
+        // half of the weight fragments is a select (wm is wave-uniform), not a
+        // branch. Tiles with a rider are the rare case: that code sits out of
+        // line.
+        __builtin_amdgcn_sched_barrier(0);
+        if (__builtin_expect(has_r, 0)) {
+#pragma unroll
+          for (int x = 0; x < RX; ++x) {
+            const bf16x8 w = (TN >= 2 && wm != 0) ? cur.w[TN >= 2 ? RX + x : 0] : cur.w[x];
+            mma(w, fr, accr[x]);
+            if constexpr (GATED) {
+              const bf16x8 u = (TN >= 2 && wm != 0) ? cur.u[TN >= 2 ? RX + x : 0] : cur.u[x];
+              mma(u, fr, accr2[x]);
+            }
+          }
+          if (RD) fr = read_r(nbuf, nks);
         }
       }
     };
@@ -402,6 +507,30 @@ struct TileGemmDL {
       }
     };
 
+    // the rider's rows: lane holds D[n = 4*lq + i][m = lr] of each 16 x 16 tile
+    auto epilogue_r = [&](const GemmTile& t) {
+      if constexpr (RIDE) {
+#pragma unroll
+        for (int x = 0; x < RX; ++x) {
+          const int n = t.n0 + wn * WTN + (xb + x) * MF + 4 * lq;
+          if (!r_wave || lr >= t.r_rows || n >= N) continue;
+          int64_t orow = t.r_crow + lr;
+          if constexpr (EPI == EPI_SLOTS_BF16)
+            orow = (int64_t)t.o_tok[orow] * t.o_k + t.o_slot[orow];
+          bf16* out = reinterpret_cast<bf16*>(Cv) + orow * ldc;
+          bf16x4 o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = accr[x][i];
+            if constexpr (GATED) v = silu_f(v) * accr2[x][i];
+            if (EPI == EPI_RELU_BF16) v = fmaxf(v, 0.0f);
+            o[i] = (bf16)v;
+          }
+          *reinterpret_cast<bf16x4*>(out + n) = o;
+        }
+      }
+    };
+
     // ---- the tile and slice loops. Global slice g sits in LDS buffer
     // g % NBUF. Fragment reads are software-pipelined across the slice
     // barrier: sub-step 1 is read while sub-step 0 is multiplied, and sub-step
@@ -422,11 +551,11 @@ struct TileGemmDL {
     auto wait_slice = [&](int t) {
       const int n = l_issued - 1 - t;
       if (NBUF >= 5 && n >= 3)
-        wait_vmcnt<(NBUF >= 5 ? 3 * LPW : 0)>();
+        wait_vmcnt<(NBUF >= 5 ? 3 * LPWR : 0)>();
       else if (NBUF >= 4 && n >= 2)
-        wait_vmcnt<(NBUF >= 4 ? 2 * LPW : 0)>();
+        wait_vmcnt<(NBUF >= 4 ? 2 * LPWR : 0)>();
       else if (NBUF >= 3 && n >= 1)
-        wait_vmcnt<(NBUF >= 3 ? LPW : 0)>();
+        wait_vmcnt<(NBUF >= 3 ? LPWR : 0)>();
       else
         wait_vmcnt<0>();
     };
@@ -443,15 +572,19 @@ struct TileGemmDL {
     // exact inside a loop body but waits for everything at a loop head that
     // outstanding reads reach through the back edge.
     for (int c_idx = 0;; ++c_idx) {
+      if constexpr (RIDE) has_r = ct.r_rows > 0;
       // upper wave row with no valid row of this tile (wave-uniform): it
-      // skips the fragment reads, MFMAs and epilogue below
-      const bool busy = !(WM == 2 && wm == 1 && ct.a_rows <= WTM);
+      // skips the fragment reads, MFMAs and epilogue below (a tile with a
+      // rider keeps every wave busy)
+      const bool busy = has_r || !(WM == 2 && wm == 1 && ct.a_rows <= WTM);
       // the tile's first slice is in LDS buffer cb
       if (busy) {
         zero_acc();
+        if (RIDE && has_r && r_wave) zero_acc_r();
         read_b(cb, 0, b0);
 #pragma unroll
         for (int y = 0; y < TM; ++y) fy[y] = read_a(cb, 0, y);
+        if (RIDE && has_r && r_wave) fr = read_r(cb, 0);
         // sub-steps 0 .. NSUB-2 of the first slice, each reading the next
         if constexpr (NSUB == 2) {
           step(Yes{}, b0, b1, cb, 1);
@@ -506,6 +639,7 @@ struct TileGemmDL {
       cb = next_buf(cb);
       ++gc;
       if (busy) epilogue(ct);
+      if (RIDE && has_r) epilogue_r(ct);
       // the load cursor has already looked up the tile after this one
       if (c_idx + 1 >= tiles_end) break;
       get(c_idx + 1, ct);

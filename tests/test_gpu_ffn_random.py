@@ -107,3 +107,40 @@ def test_leftover_pieces_with_streamed_weights(seed):
                   w1b[e:e + 1].contiguous(), w2b[e:e + 1].contiguous(), hi - lo, d, dff, 1, act)
         torch.cuda.synchronize()
         assert torch.equal(ye, y[lo:hi]), f"seed {seed}: expert {e} differs when run alone"
+
+
+@pytest.mark.parametrize("d,dff,act", [(128, 4224, "swiglu"), (256, 1024, "relu")])
+def test_remainder_rows_riding_on_full_tiles(d, dff, act):
+    """Groups of k full 256-row tiles plus s rows: when ceil(s / 16) <= k the
+    s rows ride on the expert's full tiles (16 per tile and column tile)
+    instead of forming a short tile; otherwise the short tile stays. Exact
+    multiples of 16, partial last blocks, one block per tile in every column
+    (k = ceil(s / 16)), a one-row remainder and non-riding groups sit side by
+    side. With spare rows the grid is 256 workgroups, and the 33 column tiles
+    of the first GEMM (d_ff = 4224) take the column tile past one round's
+    share, where the riders move to other tiles. Outputs against the oracle,
+    and each expert's bits against that expert run alone."""
+    G = lib()
+    rng = np.random.default_rng(7100 + d)
+    sizes = [256 * 2 + 16, 256 * 3 + 48, 256 * 5 + 64, 256 * 8 + 128, 256 + 5, 256 + 100, 60, 0,
+             256 * 4, 256 * 8 + 1, 256 * 3 + 47]
+    el = len(sizes)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(offsets[-1])
+    say(f"riders: {el} experts, rows {rows}, d {d}, d_ff {dff}, {act}, sizes {sizes}")
+    w1r = 2 * dff if act == "swiglu" else dff
+    xb = dev((rng.standard_normal((rows, d))).astype(np.float32), torch.bfloat16)
+    w1b = dev((rng.standard_normal((el, w1r, d)) * d ** -0.5).astype(np.float32), torch.bfloat16)
+    w2b = dev((rng.standard_normal((el, d, dff)) * dff ** -0.5).astype(np.float32), torch.bfloat16)
+    y = _run(G, xb, offsets, w1b, w2b, rows, d, dff, el, act, 16384)
+    torch.cuda.synchronize()
+    ref = O.grouped_ffn(host(xb), offsets, host(w1b), host(w2b), act, 0, el, rows)
+    assert_close(host(y), ref, TOL["bf16"], f"riders d {d}")
+    for e in range(el):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        ye = _run(G, xb[lo:hi].contiguous(), np.array([0, hi - lo], np.int32),
+                  w1b[e:e + 1].contiguous(), w2b[e:e + 1].contiguous(), hi - lo, d, dff, 1, act)
+        torch.cuda.synchronize()
+        assert torch.equal(ye, y[lo:hi]), f"riders d {d}: expert {e} differs when run alone"
