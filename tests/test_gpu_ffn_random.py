@@ -144,3 +144,42 @@ def test_remainder_rows_riding_on_full_tiles(d, dff, act):
                   w1b[e:e + 1].contiguous(), w2b[e:e + 1].contiguous(), hi - lo, d, dff, 1, act)
         torch.cuda.synchronize()
         assert torch.equal(ye, y[lo:hi]), f"riders d {d}: expert {e} differs when run alone"
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_remainders_match_oracle_and_per_expert_bits(seed):
+    """Groups of 0-9 full tiles plus 0-255 rows: remainders above half a tile
+    (a partial tile of their own), short remainders that ride on their
+    expert's full tiles, and short ones whose expert has too few full tiles,
+    at random widths and grid sizes. Against the oracle, and each expert's
+    bits against that expert run alone."""
+    G = lib()
+    rng = np.random.default_rng(90000 + seed)
+    el = int(rng.integers(1, 20))
+    sizes = [int(v) for v in 256 * rng.integers(0, 10, el) + rng.integers(0, 256, el)]
+    d = 64 * int(rng.integers(1, 5))
+    dff = 64 * int(rng.integers(1, 40))
+    act = "swiglu" if rng.random() < 0.6 else "relu"
+    slack = int(rng.choice([0, 4096, 16384]))
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(offsets[-1])
+    say(f"remainders seed {seed}: {el} experts, rows {rows} (+{slack} spare), d {d}, "
+        f"d_ff {dff}, {act}, sizes {sizes}")
+    if rows == 0:
+        return
+    w1r = 2 * dff if act == "swiglu" else dff
+    xb = dev(rng.standard_normal((rows, d)).astype(np.float32), torch.bfloat16)
+    w1b = dev((rng.standard_normal((el, w1r, d)) * d ** -0.5).astype(np.float32), torch.bfloat16)
+    w2b = dev((rng.standard_normal((el, d, dff)) * dff ** -0.5).astype(np.float32), torch.bfloat16)
+    y = _run(G, xb, offsets, w1b, w2b, rows, d, dff, el, act, slack)
+    torch.cuda.synchronize()
+    ref = O.grouped_ffn(host(xb), offsets, host(w1b), host(w2b), act, 0, el, rows)
+    assert_close(host(y), ref, TOL["bf16"], f"remainders seed {seed}")
+    for e in range(el):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        ye = _run(G, xb[lo:hi].contiguous(), np.array([0, hi - lo], np.int32),
+                  w1b[e:e + 1].contiguous(), w2b[e:e + 1].contiguous(), hi - lo, d, dff, 1, act)
+        torch.cuda.synchronize()
+        assert torch.equal(ye, y[lo:hi]), f"remainders seed {seed}: expert {e} differs alone"
