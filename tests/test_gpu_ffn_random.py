@@ -183,3 +183,42 @@ def test_random_remainders_match_oracle_and_per_expert_bits(seed):
                   w1b[e:e + 1].contiguous(), w2b[e:e + 1].contiguous(), hi - lo, d, dff, 1, act)
         torch.cuda.synchronize()
         assert torch.equal(ye, y[lo:hi]), f"remainders seed {seed}: expert {e} differs alone"
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_remainders_gathered_rows_give_the_same_bits(seed):
+    """The gathered first GEMM (token rows read from h through src_token) on
+    random remainder layouts, riding and leftover tiles included: bitwise
+    equal to the copying path on the rows copied into expert order."""
+    G = lib()
+    rng = np.random.default_rng(91000 + seed)
+    el = int(rng.integers(1, 16))
+    sizes = [int(v) for v in 256 * rng.integers(0, 8, el) + rng.integers(0, 256, el)]
+    d = 64 * int(rng.integers(1, 4))
+    dff = 64 * int(rng.integers(1, 24))
+    act = "swiglu" if rng.random() < 0.6 else "relu"
+    slack = int(rng.choice([0, 4096, 16384]))
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(offsets[-1])
+    say(f"gathered remainders seed {seed}: {el} experts, rows {rows} (+{slack}), d {d}, "
+        f"d_ff {dff}, {act}, sizes {sizes}")
+    if rows == 0:
+        return
+    R = rows + slack
+    w1r = 2 * dff if act == "swiglu" else dff
+    h = dev(rng.standard_normal((R, d)).astype(np.float32), torch.bfloat16)
+    src = np.zeros(R, np.int32)
+    src[:rows] = rng.permutation(R)[:rows]
+    w1b = dev((rng.standard_normal((el, w1r, d)) * d ** -0.5).astype(np.float32), torch.bfloat16)
+    w2b = dev((rng.standard_normal((el, d, dff)) * dff ** -0.5).astype(np.float32), torch.bfloat16)
+    desc = G.make_desc(R, d, el, 1, dff, "bf16", "softmax", act, max_rows=R)
+    ws = G.alloc_workspace(desc)
+    off = dev(offsets)
+    src_d = dev(src)
+    y_g = torch.zeros((R, d), dtype=torch.bfloat16, device="cuda")
+    G.grouped_ffn_gather(desc, h, src_d, off, w1b, w2b, y_g, ws)
+    x_perm = h[src_d.long()].contiguous()
+    y_c = torch.zeros((R, d), dtype=torch.bfloat16, device="cuda")
+    G.grouped_ffn(desc, x_perm, off, w1b, w2b, y_c, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_g[:rows], y_c[:rows]), f"gathered remainders seed {seed}: bits differ"
