@@ -435,15 +435,51 @@ def dedup_bench(G, desc, h, b, w1, w2, ws, reps=10):
     return info
 
 
-def routing_report(cfg, b, capacity, eb):
+def router_margin_report(cfg, logits, h, wr, bias):
+    """Router margin (the gap between each token's k-th and (k+1)-th score,
+    "How Does Mixture-of-Experts Routing Affect LLM Repeatability?", router-
+    margin passage) of the step's float32 scores, and what the float32
+    rounding did to the routing: the scores recomputed in float64 from the
+    same bf16 or float32 operands (a plain torch product, outside the step),
+    the largest score error, the tokens whose top-k set differs between the
+    two, and the tokens whose float64 margin is within twice that error (the
+    near ties a differently rounded router could order otherwise). Reporting
+    only: no part of the step."""
+    import torch
+    k, E = cfg.k, cfg.E
+    if k >= E:
+        return None
+    vals, _ = torch.topk(logits, k + 1, dim=1)
+    margin = (vals[:, k - 1] - vals[:, k]).double()
+    exact = h.double() @ wr.double()
+    if bias is not None:
+        exact = exact + bias.double()[None, :]
+    err = float((logits.double() - exact).abs().max())
+    v64, i64 = torch.topk(exact, k + 1, dim=1)
+    _, i32 = torch.topk(logits, k, dim=1)
+    set32 = torch.sort(i32, dim=1).values
+    set64 = torch.sort(i64[:, :k], dim=1).values
+    flips = int((set32 != set64).any(dim=1).sum())
+    m64 = v64[:, k - 1] - v64[:, k]
+    q = torch.quantile(margin.float().cpu(), torch.tensor([0.01, 0.5])).tolist()
+    return {"kth_minus_next_min": float(margin.min()), "kth_minus_next_p01": q[0],
+            "kth_minus_next_median": q[1], "score_err_max_vs_f64": err,
+            "topk_set_differs_from_f64": flips,
+            "near_ties_f64_margin_within_2err": int((m64 <= 2 * err).sum())}
+
+
+def routing_report(cfg, b, capacity, eb, h=None, wr=None, bias=None):
     """The step's routing population: assignments per expert, rows kept and
-    dropped per expert (capacity mode), and for an expert-parallel share the
-    rows, payload bytes and message count of each destination's segment."""
+    dropped per expert (capacity mode), the router margin, and for an
+    expert-parallel share the rows, payload bytes and message count of each
+    destination's segment."""
     counts = b.counts.cpu().numpy().astype(np.int64)
     kept = counts if capacity < 0 else np.minimum(counts, capacity)
     rep = {"counts_per_expert": counts.tolist(), "kept_per_expert": kept.tolist(),
            "dropped_per_expert": (counts - kept).tolist(), "dropped": int((counts - kept).sum()),
            "empty_experts": int((counts == 0).sum())}
+    if h is not None:
+        rep["router_margin"] = router_margin_report(cfg, b.logits, h, wr, bias)
     if cfg.ep_size > 1:
         splits = b.send_splits.cpu().numpy().astype(np.int64)
         remote = [r for r in range(cfg.ep_size) if r != cfg.ep_rank]
@@ -639,7 +675,7 @@ def main():
                 (permute_bytes + combine_bytes) / ((st_ms[1] + st_ms[3]) / 1e3) / 1e9 / HBM_PEAK_GBS,
             "rows_kept": n_kept, "rows_local": n_local, "flags": flags,
         },
-        "routing": routing_report(cfg, b, capacity, eb),
+        "routing": routing_report(cfg, b, capacity, eb, h, wr, bias),
         "timing": {"mall": "evicted before every timed step (512 MiB write outside the "
                            "step's events)",
                    "value_from": "sum of the timed steps' event durations",
