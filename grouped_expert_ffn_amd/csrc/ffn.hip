@@ -205,7 +205,12 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm_dl_kernel(
     bf16* __restrict__ C, const int4* __restrict__ tiles, const int* __restrict__ n_mt_ptr,
     int N, int K, int64_t w_stride, int n_n, int64_t ldc, const int32_t* __restrict__ o_tok,
     const int32_t* __restrict__ o_slot, int o_k) {
-  using TG = TileGemmDL<BM, BN, WM, WN, EPI, BK, MF, GA, 2, RIDE>;
+  // two slice buffers, or three where they fit in the 160 KiB of LDS (the
+  // 128-wide tile without the gated pair: 48 KiB slices, so a third one
+  // gives each slice two slices of MFMAs to arrive)
+  using TG2 = TileGemmDL<BM, BN, WM, WN, EPI, BK, MF, GA, 2, RIDE>;
+  using TG = TileGemmDL<BM, BN, WM, WN, EPI, BK, MF, GA,
+                        TG2::LDS_BUF * 2 * 3 <= 160 * 1024 ? 3 : 2, RIDE>;
   __shared__ __attribute__((aligned(1024))) bf16 lds[TG::LDS_ELEMS];
   const int n_m = *n_mt_ptr;
   const int G = gridDim.x;
