@@ -2,13 +2,16 @@
 count, widths, expert count, k, activation, gate form, dtype, capacity,
 expert-parallel share and router bias all drawn per case. Each case checks the
 copying path against the oracle (routing and plan bit-exact, y within
-tolerance of the per-token oracle on the GPU's routing) and the gathered and
-slot-ordered paths bitwise against it."""
+tolerance of the per-token oracle on the GPU's routing), the gathered and
+slot-ordered paths bitwise against it, and the deduplicated expert-parallel
+packing against the oracle, with the local experts run from its pair rows
+bitwise equal to the plain path's rows."""
 import numpy as np
 import pytest
 import torch
 
-from tests.gpu_util import lib, run_layer, say, upload_layer
+from tests.gpu_util import host, lib, run_layer, say, upload_layer
+from tests.test_gpu_dedup import _check_pack, _pack
 from tests.test_gpu_layer import _check_layer
 from workloads import LayerConfig, make_inputs
 
@@ -60,3 +63,11 @@ def test_random_layer_against_oracle_and_fused_paths(seed):
     G.combine_slots(desc, ys, bufs.topk_idx, bufs.topk_gate, bufs.dest, y3)
     torch.cuda.synchronize()
     assert torch.equal(y3, y), "slot path"
+    # one send row per (destination rank, token) pair, and the experts run from those rows
+    out = _pack(G, desc, dv["h"], bufs.topk_idx, bufs, ws)
+    _, lo, hi = _check_pack(desc, dv["h"], host(bufs.topk_idx), bufs, out)
+    y4 = torch.zeros_like(bufs.y_perm)
+    G.grouped_ffn_gather(desc, out["send_buf"], out["recv_rows"], bufs.offsets, dv["w1"],
+                         dv["w2"], y4, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y4[lo:hi], bufs.y_perm[lo:hi]), "experts run from the pair rows"
