@@ -222,3 +222,58 @@ def test_random_remainders_gathered_rows_give_the_same_bits(seed):
     G.grouped_ffn(desc, x_perm, off, w1b, w2b, y_c, ws)
     torch.cuda.synchronize()
     assert torch.equal(y_g[:rows], y_c[:rows]), f"gathered remainders seed {seed}: bits differ"
+
+
+# wide layers with many ragged experts: several rounds of the persistent grid,
+# riders, short tiles and leftover launches; seed 91011 draws 682 MiB of
+# weights, past the 256 MiB last-level cache, so its leftover pieces load
+# their weights non-temporal
+@pytest.mark.parametrize("seed", [91000, 91001, 91002, 91003, 91011])
+def test_wide_random_layouts_sampled_rows_and_per_expert_bits(seed):
+    G = lib()
+    rng = np.random.default_rng(seed)
+    el = int(rng.integers(1, 40))
+    full = rng.integers(0, 12, el)
+    rem = rng.integers(0, 256, el)
+    sizes = [int(v) for v in 256 * full + rem]
+    d = 256 * int(rng.integers(1, 9))
+    dff = 256 * int(rng.integers(1, 17))
+    act = "swiglu" if rng.random() < 0.7 else "relu"
+    slack = int(rng.choice([0, 1000]))
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(offsets[-1])
+    w1r = 2 * dff if act == "swiglu" else dff
+    say(f"seed {seed}: {el} experts, rows {rows} (+{slack} spare), d {d}, d_ff {dff}, {act}, "
+        f"weights {el * (w1r + dff) * d * 2 / 2 ** 20:.0f} MiB")
+    if rows == 0:
+        return
+    xb = dev(rng.standard_normal((rows, d)).astype(np.float32), torch.bfloat16)
+    w1b = dev((rng.standard_normal((el, w1r, d)) * d ** -0.5).astype(np.float32), torch.bfloat16)
+    w2b = dev((rng.standard_normal((el, d, dff)) * dff ** -0.5).astype(np.float32), torch.bfloat16)
+    y = _run(G, xb, offsets, w1b, w2b, rows, d, dff, el, act, slack)
+    torch.cuda.synchronize()
+    # the first and last row of every 256-row tile, each expert's last rows, random rows
+    pick = set(rng.choice(rows, size=min(rows, 128), replace=False).tolist())
+    for e in range(el):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        for r in range(lo, hi, 256):
+            pick.update({r, min(r + 255, hi - 1)})
+        if hi > lo:
+            pick.update(range(max(lo, hi - 3), hi))
+    pick = np.array(sorted(pick), np.int64)
+    xs, w1s, w2s = host(xb), host(w1b), host(w2b)
+    e_of = np.searchsorted(offsets.astype(np.int64), pick, side="right") - 1
+    want = np.zeros((pick.size, d))
+    for e in np.unique(e_of):
+        m = e_of == e
+        want[m] = O.expert_ffn(xs[pick[m]], w1s[e], w2s[e], act)
+    assert_close(host(y[torch.as_tensor(pick, device="cuda")]), want, TOL["bf16"],
+                 f"seed {seed}: sampled rows")
+    for e in range(el):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        ye = _run(G, xb[lo:hi].contiguous(), np.array([0, hi - lo], np.int32),
+                  w1b[e:e + 1].contiguous(), w2b[e:e + 1].contiguous(), hi - lo, d, dff, 1, act)
+        torch.cuda.synchronize()
+        assert torch.equal(ye, y[lo:hi]), f"seed {seed}: expert {e} differs when run alone"
