@@ -12,7 +12,8 @@
 //
 // The MFMA is issued as D = W . X^T (weights as the first operand), so each
 // lane ends up holding four consecutive output columns of one row: stores of
-// the epilogue are 8-byte (bf16) or 16-byte (fp32) vectors.
+// the epilogue are 16-byte vectors (bf16, after a lane swap between column
+// tiles; 8-byte where a wave has a single column tile) or fp32 vectors.
 #pragma once
 
 #include <type_traits>
@@ -471,7 +472,55 @@ struct TileGemmDL {
     // ---- epilogue: lane holds D[n][m = lr] for n = 8*g + 4*lq + i (32x32
     // tiles, g = 0..3) or n = 4*lq + i (16x16 tiles), four consecutive
     // columns at a time
+    // one 16x16 tile's four columns of this lane as bf16 (activation applied),
+    // packed in two 32-bit words
+    auto pack4 = [&](int x, int y, uint32_t* p) {
+      bf16x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = acc[x][y][i];
+        if (GATED) v = silu_f(v) * acc2[GATED ? x : 0][GATED ? y : 0][i];
+        if (EPI == EPI_RELU_BF16) v = fmaxf(v, 0.0f);
+        o[i] = (bf16)v;
+      }
+      __builtin_memcpy(p, &o, 8);
+    };
     auto epilogue = [&](const GemmTile& t) {
+      // bf16 outputs of 16x16 tiles, column tiles in pairs: the lane-swap
+      // instruction trades the four columns that lanes of 16-lane row q hold
+      // of tile x+1 (q even) against those of tile x (q odd) with the
+      // neighbouring row, so that each lane holds eight consecutive columns:
+      // row 0 columns 0-7 of tile x, row 1 columns 0-7 of tile x+1, rows 2
+      // and 3 columns 8-15 of each. One 16-byte store then covers 16 output
+      // rows by 64 bytes, half the store instructions of 8-byte stores (the
+      // store burst at the end of a tile is what short-K GEMMs wait for).
+      // Every lane takes part in the swaps; rows past a_rows only skip the
+      // store. The values are the same conversions, so the bits are too.
+      if constexpr (EPI != EPI_ROUTER_F32 && MF == 16 && TN % 2 == 0) {
+#pragma unroll
+        for (int y = 0; y < TM; ++y) {
+          const int m = wm * WTM + y * MF + lr;
+          const bool row_ok = m < t.a_rows;
+          int64_t orow = t.c_row + m;
+          if constexpr (EPI == EPI_SLOTS_BF16)
+            orow = row_ok ? (int64_t)t.o_tok[orow] * t.o_k + t.o_slot[orow] : 0;
+          bf16* out = reinterpret_cast<bf16*>(Cv) + orow * ldc;
+#pragma unroll
+          for (int p = 0; p < TN / 2; ++p) {
+            uint32_t pa[2], pb[2];
+            pack4(2 * p, y, pa);
+            pack4(2 * p + 1, y, pb);
+            const auto s0 = __builtin_amdgcn_permlane16_swap(pa[0], pb[0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(pa[1], pb[1], false, false);
+            const int n = t.n0 + wn * WTN + (2 * p + (lq & 1)) * MF + 8 * (lq >> 1);
+            if (row_ok && n < N) {
+              const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+              *reinterpret_cast<u32x4*>(out + n) = v;
+            }
+          }
+        }
+        return;
+      }
 #pragma unroll
       for (int y = 0; y < TM; ++y) {
         const int m = wm * WTM + y * MF + lr;
